@@ -1,0 +1,10 @@
+"""Seeded synthetic inputs shared by the CPU oracle and the HIP path.
+
+This package holds no arithmetic of the attention method itself: it only draws
+random video-latent Q/K/V tensors, audio-to-video norm maps and upstream
+gradients with the structure the Prism pages describe (static background,
+directional content variation, compact sounding regions), and rounds them to
+bfloat16.
+"""
+
+from .generator import CONFIGS, WorkloadConfig, generate, bf16_round, bf16_bits_to_f32  # noqa: F401
