@@ -1,0 +1,274 @@
+"""Benchmark of one Prism dynamic sparse video self-attention layer on one MI355X.
+
+A step is one pass of the whole layer over the 2K headline workload (latent
+grid 32 x 88 x 160 = 450,560 video tokens, 2 heads of 128 channels, bf16,
+top-k 16, top-p 0.9, density cap 10%): zone statistics, shape planning,
+permutation + pooled block selection, sparse forward and sparse backward.
+Inputs are seeded synthetic tensors already resident in HBM.
+
+Prints one JSON line: fwd+bwd milliseconds per head (the whole layer), the
+achieved MFMA TFLOP/s of the attention kernels, a roofline entry for the
+dominant kernel (HIP-event timed), the in-house dense flash attention on the
+same inputs, and the CPU oracle timed on a bounded sample.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload 2k]
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
+PEAK_HBM_GBS = 8000.0
+
+
+def log(*a):
+    print(f"[bench {time.strftime('%H:%M:%S')}]", *a, file=sys.stderr, flush=True)
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="2k")
+    ap.add_argument("--no-dense", action="store_true", help="skip the dense flash-attention baseline")
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--cpu-budget", type=float, default=20.0, help="target seconds of CPU oracle work")
+    return ap.parse_args()
+
+
+def selected_pairs(layer) -> list[int]:
+    import numpy as np
+    out = []
+    for ix in layer.index_host():
+        sizes = np.diff(ix["blk_start"]) * 64
+        rows = np.repeat(np.arange(sizes.size), np.diff(ix["row_ptr"]))
+        out.append(int((sizes[rows] * sizes[ix["col_idx"]]).sum()))
+    return out
+
+
+def cpu_baseline(wl, params_o, pairs_per_head, budget_s: float) -> dict:
+    """The oracle as it stands, on the host cores, on a bounded sample of the
+    same workload, scaled to milliseconds per head of the whole layer."""
+    import numpy as np
+
+    import oracle as O
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([d.get("num_threads", 1) for d in threadpool_info()] + [1])
+    except Exception:  # pragma: no cover
+        threads = 1
+    cores = len(os.sched_getaffinity(0))
+    c = wl.cfg
+    h = 0
+    v = wl.f32("v")[h:h + 1]
+    t0 = time.perf_counter()
+    zs = O.zone_statistics(v, wl.a, c.T, c.H, c.W, params_o.eps)
+    plan = O.plan_shapes(zs["g"], zs["rho"], params_o.tau128, params_o.tau256)
+    perm, bs = O.partition(plan["shape_id"][0], c.T, c.H, c.W)
+    t_plan = time.perf_counter() - t0
+    qp = O.permute_tokens(wl.f32("q")[h], perm)
+    kp = O.permute_tokens(wl.f32("k")[h], perm)
+    vp = O.permute_tokens(wl.f32("v")[h], perm)
+    dop = O.permute_tokens(wl.f32("do")[h], perm)
+    nb = bs.size - 1
+    rng = np.random.default_rng(0)
+    # selection on a row sample
+    t0 = time.perf_counter()
+    qbar, kbar = O.pool_blocks(qp, bs), O.pool_blocks(kp, bs)
+    t_pool = time.perf_counter() - t0
+    rows = rng.choice(nb, min(nb, 48), replace=False)
+    t0 = time.perf_counter()
+    sel = O.select_blocks(qp, kp, bs, params_o, c.N, rows=rows)
+    t_sel = time.perf_counter() - t0 - t_pool   # select_blocks pools again
+    t_sel_per_row = max(t_sel, 1e-9) / rows.size
+    # attention forward + backward on the sampled query blocks, until the budget
+    sizes = np.diff(bs) * 64
+    t_attn, pairs_done, done = 0.0, 0, 0
+    scale = params_o.score_scale(c.head_dim)
+    for i in rows:
+        cols = sel["rows"][int(i)]["cols"]
+        rp = np.zeros(nb + 1, np.int64)
+        rp[i + 1:] = cols.size
+        t0 = time.perf_counter()
+        op_, lse = O.sparse_attention_fwd(qp, kp, vp, bs, rp, cols, scale, rows=[int(i)])
+        O.sparse_attention_bwd(qp, kp, vp, op_, dop, lse, bs, rp, cols, scale, rows=[int(i)])
+        t_attn += time.perf_counter() - t0
+        pairs_done += int(sizes[i] * sizes[cols].sum())
+        done += 1
+        if t_attn + t_plan + t_sel > budget_s:
+            break
+    t_attn_full = t_attn / max(pairs_done, 1) * pairs_per_head
+    ms_per_head = 1e3 * (t_plan + t_pool + t_sel_per_row * nb + t_attn_full)
+    return dict(value=round(ms_per_head, 1), unit="ms/head", cores=threads, host_cpus=cores, kind="oracle",
+                sample=(f"head 0: full zone statistics, shapes and partition; pooled scores and selection of "
+                        f"{rows.size} of {nb} query-block rows; float64 forward+backward of {done} query blocks "
+                        f"({pairs_done} of {pairs_per_head} token pairs); scaled by rows and pairs"),
+                seconds_measured=round(t_plan + t_pool + t_sel + t_attn, 2))
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this build runs on one GPU; multi-GPU sharding is described in the design "
+                                   "notes but not implemented", "n_gpus": args.gpus}))
+        sys.exit(2)
+    import numpy as np
+    import torch
+
+    from dynamic_block_sparse_macro_amd import binding as B
+    from dynamic_block_sparse_macro_amd.pipeline import DenseAttention, LayerShape, PrismLayer
+    from workload import CONFIGS, generate
+
+    B.load_library()
+    cfg = CONFIGS[args.workload]
+    log("generating", cfg.name, cfg.note)
+    wl = generate(cfg)
+    shape = LayerShape(cfg.T, cfg.H, cfg.W, cfg.heads, cfg.head_dim)
+    par = B.make_params(top_k=cfg.top_k, top_p=cfg.top_p, density_cap=cfg.density_cap)
+    dev = torch.device("cuda:0")
+
+    def tdev(bits):
+        return torch.from_numpy(bits.view(np.int16)).to(dev).view(torch.bfloat16)
+
+    q, k, v, do = (tdev(b) for b in (wl.q_bits, wl.k_bits, wl.v_bits, wl.do_bits))
+    a = torch.from_numpy(wl.a).to(dev)
+    o = torch.empty_like(q)
+    dq, dk, dv = (torch.empty_like(q) for _ in range(3))
+    layer = PrismLayer(shape, par, device=dev)
+    stream = torch.cuda.current_stream(dev)
+
+    names = ["zone_stats", "plan_shapes", "select_blocks", "attn_fwd", "attn_bwd"]
+
+    def step(ev=None):
+        marks = [None] * 6
+        if ev is not None:
+            ev[0].record(stream)
+        layer.zone_stats(v, a)
+        if ev is not None:
+            ev[1].record(stream)
+        layer.plan_shapes()
+        if ev is not None:
+            ev[2].record(stream)
+        layer.select_blocks(q, k, v)
+        if ev is not None:
+            ev[3].record(stream)
+        layer.attn_fwd(o)
+        if ev is not None:
+            ev[4].record(stream)
+        layer.attn_bwd(o, do, dq, dk, dv)
+        if ev is not None:
+            ev[5].record(stream)
+        return marks
+
+    log("warmup", args.warmup)
+    for _ in range(max(args.warmup, 1)):
+        step()
+    torch.cuda.synchronize()
+    pairs = selected_pairs(layer)
+    nnz = [int(x) for x in layer.nnz]
+    nb = [int(x) for x in layer.n_blocks.cpu()]
+
+    log("timing", args.steps, "steps")
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(6)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    start.record(stream)
+    for s in range(args.steps):
+        step(evs[s])
+    end.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    total_ms = start.elapsed_time(end)
+    ms_step = total_ms / args.steps
+    stage_ms = {n: float(np.mean([e[i].elapsed_time(e[i + 1]) for e in evs])) for i, n in enumerate(names)}
+    heads, D = cfg.heads, cfg.head_dim
+    P = sum(pairs)
+    f_fwd, f_bwd = 4 * D * P, 10 * D * P
+    fwd_tflops = f_fwd / (stage_ms["attn_fwd"] * 1e-3) / 1e12
+    bwd_tflops = f_bwd / (stage_ms["attn_bwd"] * 1e-3) / 1e12
+    attn_tflops = (f_fwd + f_bwd) / ((stage_ms["attn_fwd"] + stage_ms["attn_bwd"]) * 1e-3) / 1e12
+    density = P / (heads * cfg.N ** 2)
+    log(f"step {ms_step:.2f} ms; stages {json.dumps({k: round(v, 3) for k, v in stage_ms.items()})}")
+    log(f"density {density:.4f}, attention {attn_tflops:.1f} TFLOP/s (fwd {fwd_tflops:.1f}, bwd {bwd_tflops:.1f})")
+
+    dense = None
+    if not args.no_dense:
+        log("dense baseline")
+        dn = DenseAttention(shape, par, device=dev)
+        od = torch.empty_like(q)
+        dn.forward(q, k, v, od)
+        dn.backward(q, k, v, od, do, dq, dk, dv)
+        torch.cuda.synchronize()
+        e = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+        e[0].record(stream)
+        dn.forward(q, k, v, od)
+        e[1].record(stream)
+        dn.backward(q, k, v, od, do, dq, dk, dv)
+        e[2].record(stream)
+        torch.cuda.synchronize()
+        dfwd, dbwd = e[0].elapsed_time(e[1]), e[1].elapsed_time(e[2])
+        fd = 14 * D * heads * cfg.N ** 2
+        dense = dict(fwd_ms=round(dfwd, 2), bwd_ms=round(dbwd, 2), ms_per_head=round((dfwd + dbwd) / heads, 2),
+                     tflops=round(fd / ((dfwd + dbwd) * 1e-3) / 1e12, 1))
+        log("dense", dense)
+
+    cpu = None
+    if not args.no_cpu:
+        import oracle as O
+        log("cpu oracle sample")
+        po = O.Params(top_k=cfg.top_k, top_p=cfg.top_p, density_cap=cfg.density_cap)
+        cpu = cpu_baseline(wl, po, pairs[0], args.cpu_budget)
+        log("cpu", cpu)
+
+    fwd_ms = stage_ms["attn_fwd"]
+    roof = dict(bound="mfma", kernel="attn_fwd_kernel<128,sparse>", achieved=round(fwd_tflops, 1),
+                peak=PEAK_BF16_TFLOPS, unit="TFLOP/s", frac=round(fwd_tflops / PEAK_BF16_TFLOPS, 4), traffic=None,
+                flops_per_launch=f_fwd, launch_ms=round(fwd_ms, 4))
+    line = {
+        "metric": "fwd+bwd ms per head at 450K tokens; achieved MFMA TFLOP/s (% of peak)",
+        "value": round(ms_step / heads, 3),
+        "unit": "ms/head",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 3),
+        "higher_is_better": False,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded generator: static background, directional zone fields, sound blobs)",
+        "config": {"workload": f"{cfg.note}: grid {cfg.T}x{cfg.H}x{cfg.W}, {heads} heads, head_dim {D}, "
+                               f"top-k {cfg.top_k}, top-p {cfg.top_p}, density cap {cfg.density_cap}",
+                   "tokens": cfg.N, "heads": heads, "head_dim": D, "parallelism": "single GPU"},
+        "attention_tflops": round(attn_tflops, 1),
+        "attention_pct_peak": round(100 * attn_tflops / PEAK_BF16_TFLOPS, 2),
+        "fwd_tflops": round(fwd_tflops, 1),
+        "bwd_tflops": round(bwd_tflops, 1),
+        "stage_ms": {k: round(v, 3) for k, v in stage_ms.items()},
+        "selected_density": round(density, 5),
+        "n_blocks": nb,
+        "nnz_block_pairs": nnz,
+        "token_pairs": pairs,
+        "roofline": roof,
+        "dense_baseline": dense,
+        "speedup_vs_dense": (round(dense["ms_per_head"] / (ms_step / heads), 2) if dense else None),
+        "cpu_baseline": cpu,
+        "wall_s_timed": round(wall, 3),
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,255 @@
+// C ABI of the Prism library: argument validation, workspace sizing and
+// stream-ordered orchestration of the kernels.  Every argument is checked
+// before the first HIP call, so a rejected call launches and writes nothing.
+
+#include <math.h>
+#include <stdint.h>
+#include <string.h>
+
+#include "prism_internal.h"
+
+using prism::Geometry;
+
+namespace {
+
+constexpr int64_t kMaxTokens = 65535LL * 64;  // block indices fit 16 bits
+
+int check_problem(const prism_problem* pr, Geometry* g) {
+  if (!pr) return PRISM_EINVAL;
+  if (pr->T <= 0 || pr->H <= 0 || pr->W <= 0 || pr->T % 8 || pr->H % 8 || pr->W % 8) return PRISM_EGRID;
+  if (pr->heads < 1) return PRISM_EINVAL;
+  if (pr->head_dim != 64 && pr->head_dim != 128) return PRISM_EDIM;
+  if (pr->token_stride < pr->head_dim || pr->token_stride % 8 || pr->head_stride < 0 || pr->head_stride % 8)
+    return PRISM_EINVAL;
+  const int64_t N = (int64_t)pr->T * pr->H * pr->W;
+  if (N > kMaxTokens) return PRISM_EINVAL;
+  if ((int64_t)pr->heads * N > (int64_t)INT32_MAX / 2) return PRISM_EINVAL;
+  g->T = pr->T;
+  g->H = pr->H;
+  g->W = pr->W;
+  g->heads = pr->heads;
+  g->D = pr->head_dim;
+  g->N = N;
+  g->Z = N / 512;
+  g->tiles = N / 64;
+  g->hstride = pr->head_stride;
+  g->tstride = pr->token_stride;
+  return PRISM_OK;
+}
+
+int check_params(const prism_params* p) {
+  if (!p) return PRISM_EINVAL;
+  if (!(p->eps > 0.0) || !isfinite(p->eps)) return PRISM_EPARAM;
+  if (!isfinite(p->tau128) || !isfinite(p->tau256) || !(p->tau256 <= p->tau128)) return PRISM_EPARAM;
+  if (p->top_k < 1) return PRISM_EPARAM;
+  if (!(p->top_p > 0.0 && p->top_p <= 1.0)) return PRISM_EPARAM;
+  if (!(p->density_cap > 0.0 && p->density_cap <= 1.0)) return PRISM_EPARAM;
+  if (!(p->scale >= 0.0) || !isfinite(p->scale)) return PRISM_EPARAM;
+  const int known = PRISM_VARIANT_FIXED_SHAPE | PRISM_VARIANT_TOPK_ONLY | PRISM_VARIANT_TOPP_ONLY |
+                    PRISM_VARIANT_VISUAL_ONLY | PRISM_VARIANT_AUDIO_ONLY | PRISM_VARIANT_RHO_MAX_AUDIO;
+  if (p->variant & ~known) return PRISM_EPARAM;
+  if ((p->variant & PRISM_VARIANT_TOPK_ONLY) && (p->variant & PRISM_VARIANT_TOPP_ONLY)) return PRISM_EPARAM;
+  if ((p->variant & PRISM_VARIANT_VISUAL_ONLY) && (p->variant & PRISM_VARIANT_AUDIO_ONLY)) return PRISM_EPARAM;
+  if ((p->variant & PRISM_VARIANT_FIXED_SHAPE) && (p->fixed_shape < 0 || p->fixed_shape > 15)) return PRISM_EPARAM;
+  return PRISM_OK;
+}
+
+#define CHECK(x)                  \
+  do {                            \
+    const int st_ = (x);          \
+    if (st_ != PRISM_OK) return st_; \
+  } while (0)
+
+#define HIPCALL(x)                              \
+  do {                                          \
+    if ((x) != hipSuccess) return PRISM_EHIP;   \
+  } while (0)
+
+size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+float attn_scale(const prism_params& p, int D) { return p.scale > 0 ? (float)p.scale : 1.0f / sqrtf((float)D); }
+
+// workspace of prism_select_blocks: tile sums (q, k), pooled means (q, k),
+// then the selection scratch
+size_t select_ws(const Geometry& g) {
+  const size_t pooled = align256(sizeof(double) * g.heads * g.tiles * g.D);
+  return 4 * pooled + prism::select_workspace_bytes(g);
+}
+
+size_t operand_bytes(const Geometry& g) { return align256(sizeof(uint16_t) * 2 * g.heads * g.N * g.D); }
+
+size_t bwd_ws(const Geometry& g) { return operand_bytes(g) + align256(sizeof(float) * g.heads * g.N); }
+
+}  // namespace
+
+extern "C" {
+
+const char* prism_strerror(int status) {
+  switch (status) {
+    case PRISM_OK: return "success";
+    case PRISM_EINVAL: return "invalid argument (NULL pointer, size or stride)";
+    case PRISM_EGRID: return "T, H and W must be positive multiples of 8";
+    case PRISM_EDIM: return "head_dim must be 64 or 128";
+    case PRISM_EPARAM: return "invalid hyper-parameter";
+    case PRISM_ECAPACITY: return "col_cap is smaller than the number of selected block pairs";
+    case PRISM_EWORKSPACE: return "workspace missing or too small";
+    case PRISM_EHIP: return "HIP runtime error";
+    default: return "unknown status";
+  }
+}
+
+int prism_zone_stats(const prism_problem* prob, const prism_params* par, const prism_bf16* v, const float* a,
+                     double* zstats, double* g, double* rho, prism_stream stream) {
+  Geometry geo;
+  CHECK(check_problem(prob, &geo));
+  CHECK(check_params(par));
+  if (!v || !zstats || !g || !rho) return PRISM_EINVAL;
+  HIPCALL(prism::launch_zone_stats(geo, *par, v, a, zstats, g, rho, (hipStream_t)stream));
+  return PRISM_OK;
+}
+
+int prism_plan_shapes(const prism_problem* prob, const prism_params* par, const double* g, const double* rho,
+                      uint8_t* shape_id, int32_t* perm, int32_t* blk_start, int32_t* n_blocks, prism_stream stream) {
+  Geometry geo;
+  CHECK(check_problem(prob, &geo));
+  CHECK(check_params(par));
+  if (!g || !rho || !shape_id || !perm || !blk_start || !n_blocks) return PRISM_EINVAL;
+  HIPCALL(prism::launch_plan_shapes(geo, *par, g, rho, shape_id, perm, blk_start, n_blocks, (hipStream_t)stream));
+  return PRISM_OK;
+}
+
+int prism_select_blocks(const prism_problem* prob, const prism_params* par, const prism_bf16* q,
+                        const prism_bf16* k, const prism_bf16* v, const int32_t* perm, const int32_t* blk_start,
+                        const int32_t* n_blocks, prism_bf16* qp, prism_bf16* kp, prism_bf16* vp, int32_t* row_ptr,
+                        int32_t* col_idx, int64_t col_cap, int32_t* t_row_ptr, int32_t* t_col_idx,
+                        int64_t* nnz_host, void* ws, size_t* ws_bytes, prism_stream stream) {
+  Geometry geo;
+  CHECK(check_problem(prob, &geo));
+  CHECK(check_params(par));
+  if (!ws_bytes) return PRISM_EINVAL;
+  const size_t need = select_ws(geo);
+  if (!ws) {
+    *ws_bytes = need;
+    return PRISM_OK;
+  }
+  if (*ws_bytes < need) return PRISM_EWORKSPACE;
+  if (!q || !k || !v || !perm || !blk_start || !n_blocks || !qp || !kp || !vp || !row_ptr || !col_idx ||
+      !t_row_ptr || !t_col_idx || !nnz_host || col_cap < 0)
+    return PRISM_EINVAL;
+  hipStream_t s = (hipStream_t)stream;
+  const size_t pooled = align256(sizeof(double) * geo.heads * geo.tiles * geo.D);
+  char* w = (char*)ws;
+  double* qsum = (double*)w;
+  double* ksum = (double*)(w + pooled);
+  double* qbar = (double*)(w + 2 * pooled);
+  double* kbar = (double*)(w + 3 * pooled);
+  char* sel = w + 4 * pooled;
+  HIPCALL(prism::launch_permute(geo, q, perm, qp, qsum, s));
+  HIPCALL(prism::launch_permute(geo, k, perm, kp, ksum, s));
+  HIPCALL(prism::launch_permute(geo, v, perm, vp, nullptr, s));
+  HIPCALL(prism::launch_pool_finalize(geo, qsum, blk_start, n_blocks, qbar, s));
+  HIPCALL(prism::launch_pool_finalize(geo, ksum, blk_start, n_blocks, kbar, s));
+  int status = PRISM_OK;
+  HIPCALL(prism::run_selection(geo, *par, blk_start, n_blocks, qbar, kbar, row_ptr, col_idx, col_cap, t_row_ptr,
+                               t_col_idx, nnz_host, sel, &status, s));
+  return status;
+}
+
+int prism_attn_fwd(const prism_problem* prob, const prism_params* par, const prism_bf16* qp, const prism_bf16* kp,
+                   const prism_bf16* vp, const int32_t* perm, const int32_t* blk_start, const int32_t* n_blocks,
+                   const int32_t* row_ptr, const int32_t* col_idx, prism_bf16* o, float* lse, prism_stream stream) {
+  Geometry geo;
+  CHECK(check_problem(prob, &geo));
+  CHECK(check_params(par));
+  if (!qp || !kp || !vp || !perm || !blk_start || !n_blocks || !row_ptr || !col_idx || !o || !lse)
+    return PRISM_EINVAL;
+  HIPCALL(prism::launch_attn_fwd(geo, attn_scale(*par, geo.D), qp, kp, vp, perm, blk_start, n_blocks, row_ptr,
+                                 col_idx, o, lse, (hipStream_t)stream));
+  return PRISM_OK;
+}
+
+int prism_attn_bwd(const prism_problem* prob, const prism_params* par, const prism_bf16* qp, const prism_bf16* kp,
+                   const prism_bf16* vp, const prism_bf16* o, const prism_bf16* dout, const float* lse,
+                   const int32_t* perm, const int32_t* blk_start, const int32_t* n_blocks, const int32_t* row_ptr,
+                   const int32_t* col_idx, const int32_t* t_row_ptr, const int32_t* t_col_idx, prism_bf16* dq,
+                   prism_bf16* dk, prism_bf16* dv, void* ws, size_t* ws_bytes, prism_stream stream) {
+  Geometry geo;
+  CHECK(check_problem(prob, &geo));
+  CHECK(check_params(par));
+  if (!ws_bytes) return PRISM_EINVAL;
+  const size_t need = bwd_ws(geo);
+  if (!ws) {
+    *ws_bytes = need;
+    return PRISM_OK;
+  }
+  if (*ws_bytes < need) return PRISM_EWORKSPACE;
+  if (!qp || !kp || !vp || !o || !dout || !lse || !perm || !blk_start || !n_blocks || !row_ptr || !col_idx ||
+      !t_row_ptr || !t_col_idx || !dq || !dk || !dv)
+    return PRISM_EINVAL;
+  hipStream_t s = (hipStream_t)stream;
+  uint16_t* dop = (uint16_t*)ws;
+  float* delta = (float*)((char*)ws + operand_bytes(geo));
+  HIPCALL(prism::launch_bwd_pre(geo, o, dout, perm, dop, delta, s));
+  HIPCALL(prism::launch_attn_bwd(geo, attn_scale(*par, geo.D), qp, kp, vp, dop, lse, delta, perm, blk_start,
+                                 n_blocks, row_ptr, col_idx, t_row_ptr, t_col_idx, dq, dk, dv, s));
+  return PRISM_OK;
+}
+
+int prism_dense_attn_fwd(const prism_problem* prob, const prism_params* par, const prism_bf16* q,
+                         const prism_bf16* k, const prism_bf16* v, prism_bf16* o, float* lse, void* ws,
+                         size_t* ws_bytes, prism_stream stream) {
+  Geometry geo;
+  CHECK(check_problem(prob, &geo));
+  CHECK(check_params(par));
+  if (!ws_bytes) return PRISM_EINVAL;
+  const size_t need = 3 * operand_bytes(geo);
+  if (!ws) {
+    *ws_bytes = need;
+    return PRISM_OK;
+  }
+  if (*ws_bytes < need) return PRISM_EWORKSPACE;
+  if (!q || !k || !v || !o || !lse) return PRISM_EINVAL;
+  hipStream_t s = (hipStream_t)stream;
+  uint16_t* qp = (uint16_t*)ws;
+  uint16_t* kp = (uint16_t*)((char*)ws + operand_bytes(geo));
+  uint16_t* vp = (uint16_t*)((char*)ws + 2 * operand_bytes(geo));
+  HIPCALL(prism::launch_permute(geo, q, nullptr, qp, nullptr, s));
+  HIPCALL(prism::launch_permute(geo, k, nullptr, kp, nullptr, s));
+  HIPCALL(prism::launch_permute(geo, v, nullptr, vp, nullptr, s));
+  HIPCALL(prism::launch_attn_fwd(geo, attn_scale(*par, geo.D), qp, kp, vp, nullptr, nullptr, nullptr, nullptr,
+                                 nullptr, o, lse, s));
+  return PRISM_OK;
+}
+
+int prism_dense_attn_bwd(const prism_problem* prob, const prism_params* par, const prism_bf16* q,
+                         const prism_bf16* k, const prism_bf16* v, const prism_bf16* o, const prism_bf16* dout,
+                         const float* lse, prism_bf16* dq, prism_bf16* dk, prism_bf16* dv, void* ws,
+                         size_t* ws_bytes, prism_stream stream) {
+  Geometry geo;
+  CHECK(check_problem(prob, &geo));
+  CHECK(check_params(par));
+  if (!ws_bytes) return PRISM_EINVAL;
+  const size_t need = 3 * operand_bytes(geo) + bwd_ws(geo);
+  if (!ws) {
+    *ws_bytes = need;
+    return PRISM_OK;
+  }
+  if (*ws_bytes < need) return PRISM_EWORKSPACE;
+  if (!q || !k || !v || !o || !dout || !lse || !dq || !dk || !dv) return PRISM_EINVAL;
+  hipStream_t s = (hipStream_t)stream;
+  const size_t ob = operand_bytes(geo);
+  uint16_t* qp = (uint16_t*)ws;
+  uint16_t* kp = (uint16_t*)((char*)ws + ob);
+  uint16_t* vp = (uint16_t*)((char*)ws + 2 * ob);
+  uint16_t* dop = (uint16_t*)((char*)ws + 3 * ob);
+  float* delta = (float*)((char*)ws + 4 * ob);
+  HIPCALL(prism::launch_permute(geo, q, nullptr, qp, nullptr, s));
+  HIPCALL(prism::launch_permute(geo, k, nullptr, kp, nullptr, s));
+  HIPCALL(prism::launch_permute(geo, v, nullptr, vp, nullptr, s));
+  HIPCALL(prism::launch_bwd_pre(geo, o, dout, nullptr, dop, delta, s));
+  HIPCALL(prism::launch_attn_bwd(geo, attn_scale(*par, geo.D), qp, kp, vp, dop, lse, delta, nullptr, nullptr, nullptr,
+                                 nullptr, nullptr, nullptr, nullptr, dq, dk, dv, s));
+  return PRISM_OK;
+}
+
+}  // extern "C"

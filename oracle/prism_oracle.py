@@ -499,16 +499,17 @@ def _key_tokens(cols: np.ndarray, blk_start: np.ndarray) -> np.ndarray:
     return np.concatenate([np.arange(blk_start[j] * 64, blk_start[j + 1] * 64) for j in cols])
 
 
-def sparse_attention_fwd(qp, kp, vp, blk_start, row_ptr, col_idx, scale):
+def sparse_attention_fwd(qp, kp, vp, blk_start, row_ptr, col_idx, scale, rows=None):
     """o_p = softmax_t(scale q_p . k_t) v_t over the tokens t of the key blocks
     in S_i, for every token p of query block i; lse_p = ln sum_t exp(...).
-    All arrays in permuted order, float64.  Returns (o_p [N][D], lse [N])."""
+    All arrays in permuted order, float64.  Returns (o_p [N][D], lse [N]);
+    with `rows`, only those query blocks are computed (the rest stay 0)."""
     qp = np.asarray(qp, np.float64)
     kp = np.asarray(kp, np.float64)
     vp = np.asarray(vp, np.float64)
     o = np.zeros_like(qp)
     lse = np.zeros(qp.shape[0])
-    for i in range(blk_start.size - 1):
+    for i in (range(blk_start.size - 1) if rows is None else rows):
         qs = slice(blk_start[i] * 64, blk_start[i + 1] * 64)
         kt = _key_tokens(col_idx[row_ptr[i]:row_ptr[i + 1]], blk_start)
         s = scale * (qp[qs] @ kp[kt].T)
@@ -520,14 +521,15 @@ def sparse_attention_fwd(qp, kp, vp, blk_start, row_ptr, col_idx, scale):
     return o, lse
 
 
-def sparse_attention_bwd(qp, kp, vp, op, dop, lse, blk_start, row_ptr, col_idx, scale):
+def sparse_attention_bwd(qp, kp, vp, op, dop, lse, blk_start, row_ptr, col_idx, scale, rows=None):
     """Gradients of sum(O * dO) with the selection held fixed ([zh/FAQ]: the
-    statistics, shapes and P_i are constants).  Returns (dq_p, dk_p, dv_p)."""
+    statistics, shapes and P_i are constants).  Returns (dq_p, dk_p, dv_p);
+    with `rows`, only the contributions of those query blocks."""
     qp, kp, vp, op, dop = (np.asarray(x, np.float64) for x in (qp, kp, vp, op, dop))
     dq = np.zeros_like(qp)
     dk = np.zeros_like(kp)
     dv = np.zeros_like(vp)
-    for i in range(blk_start.size - 1):
+    for i in (range(blk_start.size - 1) if rows is None else rows):
         qs = slice(blk_start[i] * 64, blk_start[i + 1] * 64)
         cols = col_idx[row_ptr[i]:row_ptr[i + 1]]
         kt = _key_tokens(cols, blk_start)

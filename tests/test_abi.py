@@ -1,0 +1,108 @@
+"""The C ABI without a GPU: the library loads, exports every entry point the
+header declares, and rejects bad arguments before any HIP call."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+from dynamic_block_sparse_macro_amd import binding as B
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "prism.h")
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(B.LIB_PATH):
+        from dynamic_block_sparse_macro_amd.build import build
+        build(verbose=False)
+    return B.load_library()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(prism_\w+)\s*\(", text)))
+
+
+def test_header_declares_the_entry_points():
+    names = declared_functions()
+    for n in ("prism_zone_stats", "prism_plan_shapes", "prism_select_blocks", "prism_attn_fwd", "prism_attn_bwd"):
+        assert n in names
+    assert set(names) == set(B.ENTRY_POINTS)
+
+
+def test_library_exports_every_declared_symbol(lib):
+    for n in declared_functions():
+        assert hasattr(lib, n), n
+
+
+def test_strerror(lib):
+    for code in range(-7, 1):
+        assert len(B.strerror(code)) > 3
+    assert B.strerror(-99) == "unknown status"
+
+
+P_OK = dict(T=16, H=16, W=16, heads=2, head_dim=128)
+
+
+def _prob(**kw):
+    d = dict(P_OK)
+    d.update(kw)
+    return B.make_problem(**d)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(T=12), B.PRISM_EGRID), (dict(W=0), B.PRISM_EGRID), (dict(H=-8), B.PRISM_EGRID),
+    (dict(head_dim=96), B.PRISM_EDIM), (dict(heads=0), B.PRISM_EINVAL),
+])
+def test_bad_problem(lib, kw, code):
+    st = B.prism_zone_stats(_prob(**kw), B.make_params(), 16, None, 16, 16, 16, check=False)
+    assert st == code
+
+
+def test_bad_strides(lib):
+    p = B.make_problem(16, 16, 16, 2, 128, token_stride=100)
+    assert B.prism_zone_stats(p, B.make_params(), 16, None, 16, 16, 16, check=False) == B.PRISM_EINVAL
+    p = B.make_problem(16, 16, 16, 2, 128, head_stride=-8)
+    assert B.prism_zone_stats(p, B.make_params(), 16, None, 16, 16, 16, check=False) == B.PRISM_EINVAL
+    p = B.make_problem(8, 8, 66000 * 8, 1, 64)   # more tokens than 16-bit block indices allow
+    assert B.prism_zone_stats(p, B.make_params(), 16, None, 16, 16, 16, check=False) in (B.PRISM_EINVAL,)
+
+
+@pytest.mark.parametrize("kw", [dict(eps=0.0), dict(eps=-1.0), dict(top_k=0), dict(top_p=0.0), dict(top_p=1.5),
+                                dict(density_cap=0.0), dict(density_cap=1.01), dict(tau128=0.2, tau256=0.3),
+                                dict(scale=-1.0), dict(variant=1 << 10), dict(variant=B.VARIANT_TOPK_ONLY |
+                                                                              B.VARIANT_TOPP_ONLY),
+                                dict(variant=B.VARIANT_FIXED_SHAPE, fixed_shape=16)])
+def test_bad_params(lib, kw):
+    st = B.prism_zone_stats(_prob(), B.make_params(**kw), 16, None, 16, 16, 16, check=False)
+    assert st == B.PRISM_EPARAM
+
+
+def test_null_pointers(lib):
+    assert B.prism_zone_stats(_prob(), B.make_params(), None, None, 16, 16, 16, check=False) == B.PRISM_EINVAL
+    assert B.prism_plan_shapes(_prob(), B.make_params(), 16, 16, None, 16, 16, 16, check=False) == B.PRISM_EINVAL
+    assert B.prism_attn_fwd(_prob(), B.make_params(), *([16] * 9), None, check=False) == B.PRISM_EINVAL
+
+
+def test_workspace_queries(lib):
+    prob, par = _prob(), B.make_params()
+    n = ctypes.c_size_t(0)
+    assert B.prism_select_blocks(prob, par, *([None] * 11), 0, None, None, None, None, n, check=False) == B.PRISM_OK
+    tiles = 16 * 16 * 16 // 64
+    # at least: float64 tile sums and pooled means of q and k, and a score panel
+    assert n.value >= 4 * 8 * 2 * tiles * 128 + 8 * tiles * tiles
+    small = ctypes.c_size_t(n.value - 1)
+    assert B.prism_select_blocks(prob, par, *([16] * 11), 10, 16, 16, 16, 16, small,
+                                 check=False) == B.PRISM_EWORKSPACE
+    nb = ctypes.c_size_t(0)
+    assert B.prism_attn_bwd(prob, par, *([None] * 17), nb, check=False) == B.PRISM_OK
+    assert nb.value >= 2 * 2 * 4096 * 128 * 2 + 4 * 2 * 4096
+    nd = ctypes.c_size_t(0)
+    assert B.prism_dense_attn_fwd(prob, par, None, None, None, None, None, None, nd, check=False) == B.PRISM_OK
+    assert nd.value >= 3 * 2 * 2 * 4096 * 128 * 2
+    assert B.prism_select_blocks(prob, par, *([16] * 11), -1, 16, 16, 16, 16, n, check=False) == B.PRISM_EINVAL
+    assert B.prism_attn_bwd(prob, par, *([16] * 17), None, check=False) == B.PRISM_EINVAL

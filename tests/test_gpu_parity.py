@@ -1,0 +1,163 @@
+"""GPU parity: every step of the HIP path (through the C ABI) against the CPU
+oracle on seeded workloads small enough for the oracle to run in full."""
+
+import math
+
+import numpy as np
+import pytest
+
+import oracle as O
+from workload import generate
+
+from parity_utils import (FWD_MAX_ABS, FWD_MEAN_ABS, GRAD_REL_L2, LSE_MAX_ABS, GpuRun, check_operands,
+                          check_partition, check_transpose, check_zone_stats, compare_rows, fwd_errors, log,
+                          oracle_index_to_device, oracle_params, reconcile_shapes, rel_l2)
+
+pytestmark = pytest.mark.gpu
+
+CASES = ["tiny", "one_zone", "par_d64", "par_small", "par_cap"]
+
+
+def _oracle_head(wl, plan, h, op):
+    c = wl.cfg
+    perm, bs = O.partition(plan["shape_id"][h], c.T, c.H, c.W)
+    qp = O.permute_tokens(wl.f32("q")[h], perm)
+    kp = O.permute_tokens(wl.f32("k")[h], perm)
+    sel = O.select_blocks(qp, kp, bs, op, c.N)
+    nb = bs.size - 1
+    rp, col = O.csr_from_rows([sel["rows"][i]["cols"] for i in range(nb)])
+    trp, tcol = O.csr_transpose(rp, col, nb)
+    return dict(perm=perm, blk_start=bs, sel=sel, row_ptr=rp, col_idx=col, t_row_ptr=trp, t_col_idx=tcol)
+
+
+@pytest.mark.parametrize("name", CASES)
+def test_pipeline_parity(name):
+    import torch
+    wl = generate(name)
+    c = wl.cfg
+    op = oracle_params(c)
+    log("case", name, "N", c.N, "heads", c.heads, "D", c.head_dim)
+    run = GpuRun(wl)
+    gpu = run.host()
+    log("gpu done, nnz", run.nnz)
+
+    zs = O.zone_statistics(wl.f32("v"), wl.a, c.T, c.H, c.W, op.eps)
+    check_zone_stats(gpu, zs)
+    plan = O.plan_shapes(zs["g"], zs["rho"], op.tau128, op.tau256)
+    forced, zone_ties = reconcile_shapes(gpu["shape_id"], zs, plan, op)
+    if zone_ties:
+        plan = O.plan_shapes(zs["g"], zs["rho"], op.tau128, op.tau256, forced_shape=forced)
+    log("zone stats and shapes match; tied zones:", zone_ties)
+
+    heads_o = []
+    tie_rows = alt_rows = 0
+    for h in range(c.heads):
+        ho = _oracle_head(wl, plan, h, op)
+        gidx = gpu["index"][h]
+        check_partition(gidx, ho["perm"], ho["blk_start"])
+        check_operands(run.layer, h, wl, ho["perm"])
+        st = compare_rows(gidx, ho["sel"], range(gidx["n_blocks"]))
+        tie_rows += st["tie_rows"]
+        alt_rows += st["alternative_rows"]
+        check_transpose(gidx)
+        if st["alternative_rows"] == 0:
+            np.testing.assert_array_equal(gidx["row_ptr"], ho["row_ptr"])
+            np.testing.assert_array_equal(gidx["col_idx"], ho["col_idx"])
+            np.testing.assert_array_equal(gidx["t_col_idx"], ho["t_col_idx"])
+        heads_o.append(ho)
+    log("block index matches; tie rows", tie_rows, "rows where the GPU took another tied option", alt_rows)
+
+    # attention on the oracle's own block index
+    layer = run.layer
+    oracle_index_to_device(layer, heads_o)
+    o2 = torch.empty_like(run.q)
+    layer.attn_fwd(o2)
+    if run.backward:
+        dq2, dk2, dv2 = (torch.empty_like(run.q) for _ in range(3))
+        layer.attn_bwd(o2, run.do, dq2, dk2, dv2)
+    torch.cuda.synchronize()
+    from parity_utils import bf16_dev_to_f32
+    o2h = bf16_dev_to_f32(o2)
+    lse2 = layer.lse.cpu().numpy()
+    scale = 1.0 / math.sqrt(c.head_dim)
+    for h, ho in enumerate(heads_o):
+        perm, bs = ho["perm"], ho["blk_start"]
+        qp, kp, vp = (O.permute_tokens(wl.f32(x)[h], perm) for x in ("q", "k", "v"))
+        op_, lse = O.sparse_attention_fwd(qp, kp, vp, bs, ho["row_ptr"], ho["col_idx"], scale)
+        o_ref = O.unpermute_tokens(op_, perm)
+        mx, mean = fwd_errors(o2h[h], o_ref)
+        lse_err = float(np.abs(lse2[h] - lse).max())
+        log(f"head {h}: forward max-abs {mx:.3e} mean-abs {mean:.3e} lse max-abs {lse_err:.3e}")
+        assert mx <= FWD_MAX_ABS and mean <= FWD_MEAN_ABS
+        assert lse_err <= LSE_MAX_ABS
+        if alt_rows == 0:
+            # the end-to-end run used the same index: outputs are bitwise equal
+            np.testing.assert_array_equal(gpu["o"][h], o2h[h])
+        if run.backward:
+            dop = O.permute_tokens(wl.f32("do")[h], perm)
+            grads = O.sparse_attention_bwd(qp, kp, vp, op_, dop, lse, bs, ho["row_ptr"], ho["col_idx"], scale)
+            for nm, gdev, gref in zip(("dq", "dk", "dv"), (dq2, dk2, dv2), grads):
+                err = rel_l2(bf16_dev_to_f32(gdev)[h], O.unpermute_tokens(gref, perm))
+                log(f"head {h}: {nm} relative L2 {err:.3e}")
+                assert err <= GRAD_REL_L2, nm
+
+
+def test_determinism():
+    """Two runs give bitwise equal block indices, outputs and gradients."""
+    wl = generate("par_cap")
+    a = GpuRun(wl, backward=True).host()
+    b = GpuRun(wl, backward=True).host()
+    for key in ("zstats", "g", "rho", "shape_id", "o", "lse", "dq", "dk", "dv"):
+        np.testing.assert_array_equal(a[key], b[key], err_msg=key)
+    for ia, ib in zip(a["index"], b["index"]):
+        for key in ("perm", "blk_start", "row_ptr", "col_idx", "t_row_ptr", "t_col_idx"):
+            np.testing.assert_array_equal(ia[key], ib[key], err_msg=key)
+
+
+@pytest.mark.parametrize("name", ["par_d64", "tiny"])
+def test_dense_baseline(name):
+    """The dense baseline (every key tile) against float64 full attention."""
+    import torch
+    from dynamic_block_sparse_macro_amd.pipeline import DenseAttention, LayerShape
+    from parity_utils import binding_params, bf16_dev_to_f32, to_dev
+    wl = generate(name)
+    c = wl.cfg
+    dense = DenseAttention(LayerShape(c.T, c.H, c.W, c.heads, c.head_dim), binding_params(c))
+    q, k, v, do = (to_dev(b) for b in (wl.q_bits, wl.k_bits, wl.v_bits, wl.do_bits))
+    o = torch.empty_like(q)
+    dq, dk, dv = (torch.empty_like(q) for _ in range(3))
+    dense.forward(q, k, v, o)
+    dense.backward(q, k, v, o, do, dq, dk, dv)
+    torch.cuda.synchronize()
+    scale = 1.0 / math.sqrt(c.head_dim)
+    for h in range(c.heads):
+        qh, kh, vh, doh = (wl.f32(x)[h] for x in ("q", "k", "v", "do"))
+        o_ref, lse = O.dense_attention(qh, kh, vh, scale)
+        mx, mean = fwd_errors(bf16_dev_to_f32(o)[h], o_ref)
+        assert mx <= FWD_MAX_ABS and mean <= FWD_MEAN_ABS
+        assert np.abs(dense.lse.cpu().numpy()[h] - lse).max() <= LSE_MAX_ABS
+        grads = O.dense_attention_bwd(qh, kh, vh, o_ref, doh, lse, scale)
+        for gdev, gref in zip((dq, dk, dv), grads):
+            assert rel_l2(bf16_dev_to_f32(gdev)[h], gref) <= GRAD_REL_L2
+
+
+def test_top_p_one_is_dense():
+    """p = 1 selects every block, so the sparse path equals the dense baseline."""
+    import torch
+    from dynamic_block_sparse_macro_amd.pipeline import DenseAttention, LayerShape
+    from parity_utils import binding_params, bf16_dev_to_f32
+    wl = generate("par_d64")
+    c = wl.cfg
+    run = GpuRun(wl, params=binding_params(c, top_p=1.0), backward=True)
+    nb = run.layer.n_blocks.cpu().numpy()
+    assert run.nnz == [int(x) ** 2 for x in nb]
+    dense = DenseAttention(LayerShape(c.T, c.H, c.W, c.heads, c.head_dim), binding_params(c))
+    o = torch.empty_like(run.q)
+    dense.forward(run.q, run.k, run.v, o)
+    torch.cuda.synchronize()
+    a, b = bf16_dev_to_f32(o), bf16_dev_to_f32(run.o)
+    # same keys, different accumulation order: equal up to one bf16 rounding step
+    assert (np.abs(a - b) <= 2.0 ** -7 * np.maximum(np.abs(a), np.abs(b)) + 1e-3).all()
+    np.testing.assert_allclose(dense.lse.cpu().numpy(), O.unpermute_tokens(
+        run.layer.lse.cpu().numpy()[..., None], run.layer.perm.cpu().numpy()[0].astype(np.int64))[..., 0],
+        atol=1e-4)

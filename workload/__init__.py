@@ -7,4 +7,4 @@ directional content variation, compact sounding regions), and rounds them to
 bfloat16.
 """
 
-from .generator import CONFIGS, WorkloadConfig, generate, bf16_round, bf16_bits_to_f32  # noqa: F401
+from .generator import CONFIGS, Workload, WorkloadConfig, bf16_bits_to_f32, bf16_round, generate  # noqa: F401
