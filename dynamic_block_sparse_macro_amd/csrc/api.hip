@@ -76,9 +76,9 @@ size_t select_ws(const Geometry& g) {
   return 4 * pooled + prism::select_workspace_bytes(g);
 }
 
-size_t operand_bytes(const Geometry& g) { return align256(sizeof(uint16_t) * 2 * g.heads * g.N * g.D); }
+size_t operand_bytes(const Geometry& g) { return align256(sizeof(uint16_t) * g.heads * g.N * g.D); }
 
-size_t bwd_ws(const Geometry& g) { return operand_bytes(g) + align256(sizeof(float) * g.heads * g.N); }
+size_t bwd_ws(const Geometry& g) { return operand_bytes(g) + 2 * align256(sizeof(float) * g.heads * g.N); }
 
 }  // namespace
 
@@ -189,8 +189,9 @@ int prism_attn_bwd(const prism_problem* prob, const prism_params* par, const pri
   hipStream_t s = (hipStream_t)stream;
   uint16_t* dop = (uint16_t*)ws;
   float* delta = (float*)((char*)ws + operand_bytes(geo));
-  HIPCALL(prism::launch_bwd_pre(geo, o, dout, perm, dop, delta, s));
-  HIPCALL(prism::launch_attn_bwd(geo, attn_scale(*par, geo.D), qp, kp, vp, dop, lse, delta, perm, blk_start,
+  float* lse2 = (float*)((char*)delta + align256(sizeof(float) * geo.heads * geo.N));
+  HIPCALL(prism::launch_bwd_pre(geo, o, dout, perm, lse, dop, delta, lse2, s));
+  HIPCALL(prism::launch_attn_bwd(geo, attn_scale(*par, geo.D), qp, kp, vp, dop, lse2, delta, perm, blk_start,
                                  n_blocks, row_ptr, col_idx, t_row_ptr, t_col_idx, dq, dk, dv, s));
   return PRISM_OK;
 }
@@ -243,12 +244,13 @@ int prism_dense_attn_bwd(const prism_problem* prob, const prism_params* par, con
   uint16_t* vp = (uint16_t*)((char*)ws + 2 * ob);
   uint16_t* dop = (uint16_t*)((char*)ws + 3 * ob);
   float* delta = (float*)((char*)ws + 4 * ob);
+  float* lse2 = (float*)((char*)delta + align256(sizeof(float) * geo.heads * geo.N));
   HIPCALL(prism::launch_permute(geo, q, nullptr, qp, nullptr, s));
   HIPCALL(prism::launch_permute(geo, k, nullptr, kp, nullptr, s));
   HIPCALL(prism::launch_permute(geo, v, nullptr, vp, nullptr, s));
-  HIPCALL(prism::launch_bwd_pre(geo, o, dout, nullptr, dop, delta, s));
-  HIPCALL(prism::launch_attn_bwd(geo, attn_scale(*par, geo.D), qp, kp, vp, dop, lse, delta, nullptr, nullptr, nullptr,
-                                 nullptr, nullptr, nullptr, nullptr, dq, dk, dv, s));
+  HIPCALL(prism::launch_bwd_pre(geo, o, dout, nullptr, lse, dop, delta, lse2, s));
+  HIPCALL(prism::launch_attn_bwd(geo, attn_scale(*par, geo.D), qp, kp, vp, dop, lse2, delta, nullptr, nullptr,
+                                 nullptr, nullptr, nullptr, nullptr, nullptr, dq, dk, dv, s));
   return PRISM_OK;
 }
 

@@ -42,6 +42,15 @@ __host__ __device__ constexpr ShapeTable make_shape_table() {
   return t;
 }
 
+// Operand tiles of the attention kernels are 64 rows x D bf16, row-major, with
+// the 16-byte chunk c of row r stored at chunk position swz_chunk<D>(r, c).  The
+// XOR pattern keeps both the 16-byte row reads and the 8-byte transposing reads
+// of a wave on distinct LDS banks, and the tile can be copied to LDS verbatim.
+template <int D>
+__host__ __device__ __forceinline__ constexpr int swz_chunk(int r, int c) {
+  return D == 128 ? (c ^ (((r & 7) << 1) | ((r >> 3) & 1))) : (c ^ (r & 7));
+}
+
 __device__ __forceinline__ float bf16_to_f32(uint16_t b) { return __uint_as_float(((uint32_t)b) << 16); }
 
 // float -> bf16, round to nearest even (finite inputs).

@@ -26,9 +26,9 @@ hipError_t launch_plan_shapes(const Geometry& g, const prism_params& p, const do
                               hipStream_t s);
 
 // ---- permutation, pooling and block selection (select.hip) ----
-// Gathers THW rows of x through perm (NULL = identity) into the two-part
-// operand layout; when pool_sums != NULL also writes per-tile float64
-// channel sums [heads][tiles][D].
+// Gathers THW rows of x through perm (NULL = identity) into the operand
+// layout (swizzled 64-row tiles); when pool_sums != NULL also writes per-tile
+// float64 channel sums [heads][tiles][D].
 hipError_t launch_permute(const Geometry& g, const uint16_t* x, const int32_t* perm, uint16_t* xp,
                           double* pool_sums, hipStream_t s);
 hipError_t launch_pool_finalize(const Geometry& g, const double* tile_sums, const int32_t* blk_start,
@@ -47,9 +47,9 @@ hipError_t launch_attn_fwd(const Geometry& g, float scale, const uint16_t* qp, c
                            const int32_t* n_blocks, const int32_t* row_ptr, const int32_t* col_idx, uint16_t* o,
                            float* lse, hipStream_t s);
 hipError_t launch_bwd_pre(const Geometry& g, const uint16_t* o, const uint16_t* dout, const int32_t* perm,
-                          uint16_t* dop, float* delta, hipStream_t s);
+                          const float* lse, uint16_t* dop, float* delta, float* lse2, hipStream_t s);
 hipError_t launch_attn_bwd(const Geometry& g, float scale, const uint16_t* qp, const uint16_t* kp,
-                           const uint16_t* vp, const uint16_t* dop, const float* lse, const float* delta,
+                           const uint16_t* vp, const uint16_t* dop, const float* lse2, const float* delta,
                            const int32_t* perm, const int32_t* blk_start, const int32_t* n_blocks,
                            const int32_t* row_ptr, const int32_t* col_idx, const int32_t* t_row_ptr,
                            const int32_t* t_col_idx, uint16_t* dq, uint16_t* dk, uint16_t* dv, hipStream_t s);

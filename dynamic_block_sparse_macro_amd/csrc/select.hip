@@ -23,7 +23,7 @@ namespace {
 constexpr int kPanelRows = 2048;   // score rows held in the workspace at once
 
 // ---------------------------------------------------------------------------
-// permutation into the two-part operand layout (+ float64 tile sums)
+// permutation into the operand layout (+ float64 tile sums)
 // ---------------------------------------------------------------------------
 template <int D>
 __global__ __launch_bounds__(256) void permute_kernel(Geometry g, const uint16_t* __restrict__ x,
@@ -36,30 +36,23 @@ __global__ __launch_bounds__(256) void permute_kernel(Geometry g, const uint16_t
   const int h = blockIdx.y, tid = threadIdx.x;
   const int64_t p0 = (int64_t)h * g.N + tile * kTile;
   uint16_t* rows = xp + p0 * D;
-  uint16_t* cols = xp + (int64_t)g.heads * g.N * D + p0 * D;
   for (int c = tid; c < kTile * CH; c += 256) {
     const int r = c / CH, k = c % CH;
     const int64_t n = perm ? (int64_t)perm[p0 + r] : tile * kTile + r;
     const uint4 val = *(const uint4*)(x + (int64_t)h * g.hstride + n * g.tstride + k * 8);
-    *(uint4*)(tb + r * LD + k * 8) = val;
-    *(uint4*)(rows + (int64_t)r * D + k * 8) = val;
+    *(uint4*)(rows + (int64_t)r * D + swz_chunk<D>(r, k) * 8) = val;
+    if (tile_sums) *(uint4*)(tb + r * LD + k * 8) = val;
   }
+  if (!tile_sums) return;
   __syncthreads();
-  for (int q = tid; q < D * 8; q += 256) {
-    const int c = q >> 3, r0 = (q & 7) * 8;
-    uint32_t w[4];
-#pragma unroll
-    for (int e = 0; e < 4; ++e)
-      w[e] = (uint32_t)tb[(r0 + 2 * e) * LD + c] | ((uint32_t)tb[(r0 + 2 * e + 1) * LD + c] << 16);
-    *(uint4*)(cols + c * kTile + r0) = make_uint4(w[0], w[1], w[2], w[3]);
-  }
-  if (tile_sums && tid < D) {
+  if (tid < D) {
     double s = 0.0;
     for (int r = 0; r < kTile; ++r) s += (double)bf16_to_f32(tb[r * LD + tid]);
     tile_sums[((int64_t)h * g.tiles + tile) * D + tid] = s;
   }
 }
 
+// ---------------------------------------------------------------------------
 // Block means from tile sums: Kbar_b = sum over the block's tiles / size.
 __global__ void pool_finalize_kernel(Geometry g, const double* __restrict__ tile_sums,
                                      const int32_t* __restrict__ blk_start, const int32_t* __restrict__ n_blocks,

@@ -52,7 +52,7 @@ class PrismLayer:
         self.perm = torch.empty(h, N, dtype=torch.int32, **dev)
         self.blk_start = torch.empty(h, t + 1, dtype=torch.int32, **dev)
         self.n_blocks = torch.empty(h, dtype=torch.int32, **dev)
-        self.qp = torch.empty(2, h, N, D, dtype=torch.bfloat16, **dev)
+        self.qp = torch.empty(h, N, D, dtype=torch.bfloat16, **dev)
         self.kp = torch.empty_like(self.qp)
         self.vp = torch.empty_like(self.qp)
         self.row_ptr = torch.empty(h, t + 1, dtype=torch.int32, **dev)

@@ -140,10 +140,13 @@ int prism_plan_shapes(const prism_problem *prob, const prism_params *par, const 
  *
  * q, k, v     THW bf16 inputs.
  * perm, blk_start, n_blocks   from prism_plan_shapes.
- * qp, kp, vp  bf16 operand buffers (out), each 2 * heads * N * D values:
- *             part 0 = rows in block order ((head * N + p) * D + c);
- *             part 1 = the same values as 64-token column tiles:
- *             heads*N*D + (head * N + (p & ~63)) * D + c * 64 + (p & 63).
+ * qp, kp, vp  bf16 operand buffers (out), each heads * N * D values: the
+ *             rows in block order, grouped in tiles of 64 rows; inside a tile
+ *             row r is contiguous (D values) but its 16-byte chunk c (values
+ *             8c .. 8c+7) is stored at chunk position c ^ f(r), with
+ *             f(r) = ((r & 7) << 1) | ((r >> 3) & 1) for D = 128 and
+ *             f(r) = r & 7 for D = 64.  Element (head, p, c) is therefore at
+ *             (head * N + p) * D + 8 * ((c / 8) ^ f(p % 64)) + c % 8.
  * row_ptr     int32 [heads][N/64 + 1] (out): CSR row pointers of the
  *             query-major block index, offsets into col_idx counted over
  *             all heads (head h starts at the sum of the earlier heads'

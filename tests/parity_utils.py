@@ -123,19 +123,28 @@ def check_partition(gidx: dict, perm: np.ndarray, blk_start: np.ndarray):
     np.testing.assert_array_equal(gidx["perm"], perm)
 
 
+def unswizzle_tiles(stored: np.ndarray, D: int) -> np.ndarray:
+    """Operand layout -> plain rows.  Each 64-row tile is row-major with the
+    16-byte chunk c of row r stored at chunk position c ^ f(r), f(r) =
+    ((r & 7) << 1) | ((r >> 3) & 1) for D = 128 and r & 7 for D = 64."""
+    n = stored.shape[0]
+    ch = D // 8
+    t = stored.reshape(n // 64, 64, ch, 8)
+    r = np.arange(64)
+    f = (((r & 7) << 1) | ((r >> 3) & 1)) if D == 128 else (r & 7)
+    pos = np.arange(ch)[None, :] ^ f[:, None]            # [64][ch]: stored position of logical chunk c
+    return t[:, r[:, None], pos, :].reshape(n, D)
+
+
 def check_operands(layer, h: int, wl: Workload, perm: np.ndarray):
-    """Part 0 of each operand buffer is the permuted rows, bitwise; part 1 the
-    same values as 64-token column tiles."""
-    c = wl.cfg
-    N, D = c.N, c.head_dim
+    """The operand buffers hold the permuted rows, bitwise, in the swizzled
+    64-row tile layout."""
+    import torch
+    D = wl.cfg.head_dim
     for name, buf in (("q", layer.qp), ("k", layer.kp), ("v", layer.vp)):
         bits = getattr(wl, name + "_bits")[h]
-        import torch
-        host = buf.view(torch.int16).cpu().numpy().view(np.uint16)
-        rows = host[0, h]
-        np.testing.assert_array_equal(rows, bits[perm])
-        cols = host[1, h].reshape(N // 64, D, 64)
-        np.testing.assert_array_equal(cols, rows.reshape(N // 64, 64, D).transpose(0, 2, 1))
+        host = buf.view(torch.int16).cpu().numpy().view(np.uint16)[h]
+        np.testing.assert_array_equal(unswizzle_tiles(host, D), bits[perm])
 
 
 def compare_rows(gidx: dict, osel: dict, rows) -> dict:

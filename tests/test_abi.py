@@ -100,9 +100,9 @@ def test_workspace_queries(lib):
                                  check=False) == B.PRISM_EWORKSPACE
     nb = ctypes.c_size_t(0)
     assert B.prism_attn_bwd(prob, par, *([None] * 17), nb, check=False) == B.PRISM_OK
-    assert nb.value >= 2 * 2 * 4096 * 128 * 2 + 4 * 2 * 4096
+    assert nb.value >= 2 * 4096 * 128 * 2 + 2 * 4 * 2 * 4096
     nd = ctypes.c_size_t(0)
     assert B.prism_dense_attn_fwd(prob, par, None, None, None, None, None, None, nd, check=False) == B.PRISM_OK
-    assert nd.value >= 3 * 2 * 2 * 4096 * 128 * 2
+    assert nd.value >= 3 * 2 * 4096 * 128 * 2
     assert B.prism_select_blocks(prob, par, *([16] * 11), -1, 16, 16, 16, 16, n, check=False) == B.PRISM_EINVAL
     assert B.prism_attn_bwd(prob, par, *([16] * 17), None, check=False) == B.PRISM_EINVAL

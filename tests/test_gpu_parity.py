@@ -156,8 +156,11 @@ def test_top_p_one_is_dense():
     dense.forward(run.q, run.k, run.v, o)
     torch.cuda.synchronize()
     a, b = bf16_dev_to_f32(o), bf16_dev_to_f32(run.o)
-    # same keys, different accumulation order: equal up to one bf16 rounding step
-    assert (np.abs(a - b) <= 2.0 ** -7 * np.maximum(np.abs(a), np.abs(b)) + 1e-3).all()
+    # same keys in another order: each result is within the forward bar of the
+    # exact one, so the two are within twice that bar of each other
+    mx, mean = fwd_errors(a, b.astype(np.float64))
+    log(f"sparse (p = 1) vs dense: max-abs {mx:.3e} mean-abs {mean:.3e}")
+    assert mx <= 2 * FWD_MAX_ABS and mean <= FWD_MEAN_ABS
     np.testing.assert_allclose(dense.lse.cpu().numpy(), O.unpermute_tokens(
         run.layer.lse.cpu().numpy()[..., None], run.layer.perm.cpu().numpy()[0].astype(np.int64))[..., 0],
         atol=1e-4)
