@@ -43,6 +43,7 @@ def parse():
     ap.add_argument("--no-dense", action="store_true", help="skip the dense flash-attention baseline")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--cpu-budget", type=float, default=20.0, help="target seconds of CPU oracle work")
+    ap.add_argument("--dump-index", default="", help="write the block index of the last step to this .npz")
     return ap.parse_args()
 
 
@@ -175,6 +176,10 @@ def main():
         step()
     torch.cuda.synchronize()
     pairs = selected_pairs(layer)
+    if args.dump_index:
+        ix = layer.index_host()
+        np.savez_compressed(args.dump_index, **{f"{k}_{h}": v for h, d in enumerate(ix) for k, v in d.items()
+                                                if k != "perm"})
     nnz = [int(x) for x in layer.nnz]
     nb = [int(x) for x in layer.n_blocks.cpu()]
 

@@ -29,6 +29,8 @@
 
 #include <limits.h>
 
+#include <type_traits>
+
 #include "prism_device.h"
 #include "prism_internal.h"
 
@@ -81,32 +83,50 @@ __device__ __forceinline__ void dma_vec64(char* lds, const float* __restrict__ s
   if (lane < 16) __builtin_amdgcn_global_load_lds((const void*)(src + lane * 4), (lds_void*)lds, 16, 0, 0);
 }
 
-// 16-byte operand read of row r, k-step s, lane group g (columns 16 s + 8 g .. + 7)
+// Per-lane LDS byte offsets inside an operand tile.  With the XOR swizzle of
+// swz_chunk the chunk a lane touches depends only on its row modulo 16, so one
+// set of offsets serves every 32-row block of a tile (added as immediates).
+//  row[s]    16-byte row read: row l32, columns 16 s + 8 g .. + 7 (A or B
+//            operand whose lanes index tile rows)
+//  tr[h][u]  8-byte transposing read of rows 8 h + 4 g + {0..3} (plus the
+//            32-row / 16-row block base), columns 32 u + 16 (l/16 & 1) + 4 (l%16 & 3)
+//            .. + 3: in each 16-lane group lane i then holds column
+//            32 u + 16 (l/16 & 1) + i of those four rows.
 template <int D>
-__device__ __forceinline__ bf16x8 rd_row(const char* tile, int r, int s, int g) {
-  return *(const bf16x8*)(tile + r * TileGeo<D>::ROWB + swz_chunk<D>(r, 2 * s + g) * 16);
-}
+struct LaneOff {
+  static constexpr int ROWB = D * 2;
+  int row[D / 16];
+  int tr[2][D / 32];
+  __device__ __forceinline__ void init(int lane) {
+    const int g = lane >> 5, l32 = lane & 31, gg = lane >> 4, a = lane & 15;
+#pragma unroll
+    for (int s = 0; s < D / 16; ++s) row[s] = l32 * ROWB + swz_chunk<D>(l32, 2 * s + g) * 16;
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+#pragma unroll
+      for (int u = 0; u < D / 32; ++u) {
+        const int r = 8 * h + 4 * g + (a >> 2);
+        const int col = 32 * u + 16 * (gg & 1) + 4 * (a & 3);
+        tr[h][u] = r * ROWB + swz_chunk<D>(r, col >> 3) * 16 + (col & 7) * 2;
+      }
+  }
+};
 
-// 8-byte transposing read: in each 16-lane group, lane i receives column
-// n0 + 16 (group & 1) + i of rows k0 .. k0 + 3.
+// operand whose lanes index tile rows 32 kk + l32 (k-step s over columns)
 template <int D>
-__device__ __forceinline__ short4v rd_tr(const char* tile, int n0, int k0, int lane) {
-  const int gg = lane >> 4, a = lane & 15;
-  const int r = k0 + (a >> 2);
-  const int col = n0 + 16 * (gg & 1) + 4 * (a & 3);
-  const char* p = tile + r * TileGeo<D>::ROWB + swz_chunk<D>(r, col >> 3) * 16 + (col & 7) * 2;
-  return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_short4*)p);
+__device__ __forceinline__ bf16x8 lds_row(const char* tile, const LaneOff<D>& o, int kk, int s) {
+  return *(const bf16x8*)(tile + kk * 32 * LaneOff<D>::ROWB + o.row[s]);
 }
 
 // Column operand of a 32x32x16 MFMA from a row tile: lane l takes column
-// n0 + l % 32 and, for k-step (kk, hh), rows 32 kk + 16 hh + 4 g + {0..3} and
-// the same + 8 (g = l / 32): the register order of a 32x32 accumulator used
-// as the B operand of the next product.
+// 32 u + l % 32 and, for k-step (kk, hh), rows 32 kk + 16 hh + 4 g + {0..3}
+// and the same + 8 (g = l / 32): the register order of a 32x32 accumulator
+// used as the B operand of the next product.
 template <int D>
-__device__ __forceinline__ bf16x8 rd_col(const char* tile, int n0, int kk, int hh, int lane) {
-  const int k0 = 32 * kk + 16 * hh + 4 * (lane >> 5);
-  const short4v lo = rd_tr<D>(tile, n0, k0, lane);
-  const short4v hi = rd_tr<D>(tile, n0, k0 + 8, lane);
+__device__ __forceinline__ bf16x8 lds_col(const char* tile, const LaneOff<D>& o, int u, int kk, int hh) {
+  const char* p = tile + (32 * kk + 16 * hh) * LaneOff<D>::ROWB;
+  const short4v lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_short4*)(p + o.tr[0][u]));
+  const short4v hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_short4*)(p + o.tr[1][u]));
   return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
 }
 
@@ -211,6 +231,9 @@ __device__ __forceinline__ PairIter make_iter(const Geometry& g, int h, int pair
   return it;
 }
 
+template <int B>
+using Parity = std::integral_constant<int, B>;
+
 // ---------------------------------------------------------------------------
 // forward
 // ---------------------------------------------------------------------------
@@ -231,6 +254,8 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(
   const int rloc = 32 * (w & 1) + l32;          // row within the query tile
   const uint16_t* Kb = kp + hN * D;
   const uint16_t* Vb = vp + hN * D;
+  LaneOff<D> off;
+  off.init(lane);
 
   bf16x8 qreg[D / 16];
   {
@@ -246,32 +271,33 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(
   float m_run = -INFINITY, l_run = 0.0f, r_run = 0.0f;
 
   PairIter it = make_iter(g, h, pair, blk_start, n_blocks, DENSE ? nullptr : row_ptr, col_idx);
-  int kt, kt_next;
-  bool ua, ub, ua_n, ub_n;
+  int kt, kt_next = 0;
+  bool ua, ub, ua_n = false, ub_n = false;
   bool have = it.next(kt, ua, ub);
   if (have) {
     dma_tile<D>(smem[0][0], Kb + (int64_t)kt * kTile * D);
     dma_tile<D>(smem[0][1], Vb + (int64_t)kt * kTile * D);
   }
-  int buf = 0;
-  while (have) {
+
+  auto step = [&](auto par) {
+    constexpr int B = decltype(par)::value;
     const bool have_next = it.next(kt_next, ua_n, ub_n);
     wait_dma();
     __syncthreads();
     if (have_next) {
-      dma_tile<D>(smem[buf ^ 1][0], Kb + (int64_t)kt_next * kTile * D);
-      dma_tile<D>(smem[buf ^ 1][1], Vb + (int64_t)kt_next * kTile * D);
+      dma_tile<D>(smem[B ^ 1][0], Kb + (int64_t)kt_next * kTile * D);
+      dma_tile<D>(smem[B ^ 1][1], Vb + (int64_t)kt_next * kTile * D);
     }
     if (second ? ub : ua) {
-      const char* Kt = smem[buf][0];
-      const char* Vt = smem[buf][1];
+      const char* Kt = smem[B][0];
+      const char* Vt = smem[B][1];
       floatx16 sacc[2];
 #pragma unroll
       for (int kk = 0; kk < 2; ++kk) {
 #pragma unroll
         for (int i = 0; i < 16; ++i) sacc[kk][i] = 0.0f;
 #pragma unroll
-        for (int s = 0; s < D / 16; ++s) sacc[kk] = mfma32(rd_row<D>(Kt, 32 * kk + l32, s, g32), qreg[s], sacc[kk]);
+        for (int s = 0; s < D / 16; ++s) sacc[kk] = mfma32(lds_row<D>(Kt, off, kk, s), qreg[s], sacc[kk]);
       }
       float mloc = sacc[0][0];
 #pragma unroll
@@ -307,18 +333,22 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(
       l_run += lsum;
       r_run += rsum;
 #pragma unroll
-      for (int u = 0; u < D / 32; ++u)
+      for (int kk = 0; kk < 2; ++kk)
 #pragma unroll
-        for (int kk = 0; kk < 2; ++kk)
+        for (int hh = 0; hh < 2; ++hh)
 #pragma unroll
-          for (int hh = 0; hh < 2; ++hh)
-            oacc[u] = mfma32(rd_col<D>(Vt, 32 * u, kk, hh, lane), pb[kk * 2 + hh], oacc[u]);
+          for (int u = 0; u < D / 32; ++u)
+            oacc[u] = mfma32(lds_col<D>(Vt, off, u, kk, hh), pb[kk * 2 + hh], oacc[u]);
     }
     kt = kt_next;
     ua = ua_n;
     ub = ub_n;
     have = have_next;
-    buf ^= 1;
+  };
+  while (have) {
+    step(Parity<0>{});
+    if (!have) break;
+    step(Parity<1>{});
   }
 
   const float l_tot = l_run + __shfl_xor(l_run, 32, 64);
@@ -370,10 +400,10 @@ __global__ __launch_bounds__(256) void bwd_pre_kernel(Geometry g, const uint16_t
 }
 
 // ---------------------------------------------------------------------------
-// backward, query-major pass: dQ
+// backward, query-major pass: dQ (in 32-key halves of each key tile)
 // ---------------------------------------------------------------------------
 template <int D, bool DENSE>
-__global__ __launch_bounds__(kThreads, 1) void attn_bwd_dq_kernel(
+__global__ __launch_bounds__(kThreads, 2) void attn_bwd_dq_kernel(
     Geometry g, float scale, float sl2, const uint16_t* __restrict__ qp, const uint16_t* __restrict__ kp,
     const uint16_t* __restrict__ vp, const uint16_t* __restrict__ dop, const float* __restrict__ lse2,
     const float* __restrict__ delta, const int32_t* __restrict__ perm, const int32_t* __restrict__ blk_start,
@@ -390,6 +420,8 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bwd_dq_kernel(
   const int rloc = 32 * (w & 1) + l32;
   const uint16_t* Kb = kp + hN * D;
   const uint16_t* Vb = vp + hN * D;
+  LaneOff<D> off;
+  off.init(lane);
 
   bf16x8 qreg[D / 16], dreg[D / 16];
   {
@@ -410,57 +442,56 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bwd_dq_kernel(
     for (int i = 0; i < 16; ++i) dqacc[u][i] = 0.0f;
 
   PairIter it = make_iter(g, h, pair, blk_start, n_blocks, DENSE ? nullptr : row_ptr, col_idx);
-  int kt, kt_next;
-  bool ua, ub, ua_n, ub_n;
+  int kt, kt_next = 0;
+  bool ua, ub, ua_n = false, ub_n = false;
   bool have = it.next(kt, ua, ub);
   if (have) {
     dma_tile<D>(smem[0][0], Kb + (int64_t)kt * kTile * D);
     dma_tile<D>(smem[0][1], Vb + (int64_t)kt * kTile * D);
   }
-  int buf = 0;
-  while (have) {
+  auto step = [&](auto par) {
+    constexpr int B = decltype(par)::value;
     const bool have_next = it.next(kt_next, ua_n, ub_n);
     wait_dma();
     __syncthreads();
     if (have_next) {
-      dma_tile<D>(smem[buf ^ 1][0], Kb + (int64_t)kt_next * kTile * D);
-      dma_tile<D>(smem[buf ^ 1][1], Vb + (int64_t)kt_next * kTile * D);
+      dma_tile<D>(smem[B ^ 1][0], Kb + (int64_t)kt_next * kTile * D);
+      dma_tile<D>(smem[B ^ 1][1], Vb + (int64_t)kt_next * kTile * D);
     }
     if (second ? ub : ua) {
-      const char* Kt = smem[buf][0];
-      const char* Vt = smem[buf][1];
-      floatx16 sacc[2], pacc[2];
+      const char* Kt = smem[B][0];
+      const char* Vt = smem[B][1];
 #pragma unroll
       for (int kk = 0; kk < 2; ++kk) {
+        floatx16 sacc, pacc;
 #pragma unroll
-        for (int i = 0; i < 16; ++i) sacc[kk][i] = pacc[kk][i] = 0.0f;
+        for (int i = 0; i < 16; ++i) sacc[i] = pacc[i] = 0.0f;
 #pragma unroll
         for (int s = 0; s < D / 16; ++s) {
-          sacc[kk] = mfma32(rd_row<D>(Kt, 32 * kk + l32, s, g32), qreg[s], sacc[kk]);
-          pacc[kk] = mfma32(rd_row<D>(Vt, 32 * kk + l32, s, g32), dreg[s], pacc[kk]);
+          sacc = mfma32(lds_row<D>(Kt, off, kk, s), qreg[s], sacc);
+          pacc = mfma32(lds_row<D>(Vt, off, kk, s), dreg[s], pacc);
         }
-      }
-      bf16x8 dsb[4];
-#pragma unroll
-      for (int kk = 0; kk < 2; ++kk)
+        bf16x8 dsb[2];
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
-          const float pv = fast_exp2(__builtin_fmaf(sacc[kk][i], sl2, -l2));
-          dsb[kk * 2 + (i >> 3)][i & 7] = (__bf16)(pv * (pacc[kk][i] - dlt));
+          const float pv = fast_exp2(__builtin_fmaf(sacc[i], sl2, -l2));
+          dsb[i >> 3][i & 7] = (__bf16)(pv * (pacc[i] - dlt));
         }
 #pragma unroll
-      for (int u = 0; u < D / 32; ++u)
+        for (int hh = 0; hh < 2; ++hh)
 #pragma unroll
-        for (int kk = 0; kk < 2; ++kk)
-#pragma unroll
-          for (int hh = 0; hh < 2; ++hh)
-            dqacc[u] = mfma32(rd_col<D>(Kt, 32 * u, kk, hh, lane), dsb[kk * 2 + hh], dqacc[u]);
+          for (int u = 0; u < D / 32; ++u) dqacc[u] = mfma32(lds_col<D>(Kt, off, u, kk, hh), dsb[hh], dqacc[u]);
+      }
     }
     kt = kt_next;
     ua = ua_n;
     ub = ub_n;
     have = have_next;
-    buf ^= 1;
+  };
+  while (have) {
+    step(Parity<0>{});
+    if (!have) break;
+    step(Parity<1>{});
   }
   __syncthreads();
   uint16_t* st = (uint16_t*)&smem[0][0][0];
@@ -470,7 +501,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bwd_dq_kernel(
 }
 
 // ---------------------------------------------------------------------------
-// backward, key-major pass: dK and dV
+// backward, key-major pass: dK and dV (in 32-query halves of each query tile)
 // ---------------------------------------------------------------------------
 template <int D, bool DENSE>
 __global__ __launch_bounds__(kThreads, 1) void attn_bwd_dkdv_kernel(
@@ -491,6 +522,8 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bwd_dkdv_kernel(
   const int rloc = 32 * (w & 1) + l32;
   const uint16_t* Qb = qp + hN * D;
   const uint16_t* Db = dop + hN * D;
+  LaneOff<D> off;
+  off.init(lane);
 
   bf16x8 kreg[D / 16], vreg[D / 16];
   {
@@ -509,8 +542,8 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bwd_dkdv_kernel(
     for (int i = 0; i < 16; ++i) dkacc[u][i] = dvacc[u][i] = 0.0f;
 
   PairIter it = make_iter(g, h, pair, blk_start, n_blocks, DENSE ? nullptr : t_row_ptr, t_col_idx);
-  int qt, qt_next;
-  bool ua, ub, ua_n, ub_n;
+  int qt, qt_next = 0;
+  bool ua, ub, ua_n = false, ub_n = false;
   bool have = it.next(qt, ua, ub);
   auto issue = [&](int b, int tq) {
     dma_tile<D>(smem[b][0], Qb + (int64_t)tq * kTile * D);
@@ -519,58 +552,58 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bwd_dkdv_kernel(
     if (w == 1) dma_vec64((char*)svec[b][1], delta + hN + (int64_t)tq * kTile);
   };
   if (have) issue(0, qt);
-  int buf = 0;
-  while (have) {
+  auto step = [&](auto par) {
+    constexpr int B = decltype(par)::value;
     const bool have_next = it.next(qt_next, ua_n, ub_n);
     wait_dma();
     __syncthreads();
-    if (have_next) issue(buf ^ 1, qt_next);
+    if (have_next) issue(B ^ 1, qt_next);
     if (second ? ub : ua) {
-      const char* Qt = smem[buf][0];
-      const char* Dt = smem[buf][1];
-      floatx16 sacc[2], pacc[2];
+      const char* Qt = smem[B][0];
+      const char* Dt = smem[B][1];
 #pragma unroll
       for (int qq = 0; qq < 2; ++qq) {
+        floatx16 sacc, pacc;
 #pragma unroll
-        for (int i = 0; i < 16; ++i) sacc[qq][i] = pacc[qq][i] = 0.0f;
+        for (int i = 0; i < 16; ++i) sacc[i] = pacc[i] = 0.0f;
 #pragma unroll
         for (int s = 0; s < D / 16; ++s) {
-          sacc[qq] = mfma32(rd_row<D>(Qt, 32 * qq + l32, s, g32), kreg[s], sacc[qq]);
-          pacc[qq] = mfma32(rd_row<D>(Dt, 32 * qq + l32, s, g32), vreg[s], pacc[qq]);
+          sacc = mfma32(lds_row<D>(Qt, off, qq, s), kreg[s], sacc);
+          pacc = mfma32(lds_row<D>(Dt, off, qq, s), vreg[s], pacc);
         }
-      }
-      bf16x8 pb[4], dsb[4];
-#pragma unroll
-      for (int qq = 0; qq < 2; ++qq)
+        bf16x8 pb[2], dsb[2];
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
           const int q0 = 32 * qq + 8 * j + 4 * g32;
-          const float4 l4 = *(const float4*)(&svec[buf][0][q0]);
-          const float4 d4 = *(const float4*)(&svec[buf][1][q0]);
+          const float4 l4 = *(const float4*)(&svec[B][0][q0]);
+          const float4 d4 = *(const float4*)(&svec[B][1][q0]);
           const float lv[4] = {l4.x, l4.y, l4.z, l4.w}, dvv[4] = {d4.x, d4.y, d4.z, d4.w};
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
             const int i = 4 * j + e;
-            const float pv = fast_exp2(__builtin_fmaf(sacc[qq][i], sl2, -lv[e]));
-            pb[qq * 2 + (i >> 3)][i & 7] = (__bf16)pv;
-            dsb[qq * 2 + (i >> 3)][i & 7] = (__bf16)(pv * (pacc[qq][i] - dvv[e]));
+            const float pv = fast_exp2(__builtin_fmaf(sacc[i], sl2, -lv[e]));
+            pb[i >> 3][i & 7] = (__bf16)pv;
+            dsb[i >> 3][i & 7] = (__bf16)(pv * (pacc[i] - dvv[e]));
           }
         }
 #pragma unroll
-      for (int u = 0; u < D / 32; ++u)
+        for (int hh = 0; hh < 2; ++hh)
 #pragma unroll
-        for (int qq = 0; qq < 2; ++qq)
-#pragma unroll
-          for (int hh = 0; hh < 2; ++hh) {
-            dvacc[u] = mfma32(rd_col<D>(Dt, 32 * u, qq, hh, lane), pb[qq * 2 + hh], dvacc[u]);
-            dkacc[u] = mfma32(rd_col<D>(Qt, 32 * u, qq, hh, lane), dsb[qq * 2 + hh], dkacc[u]);
+          for (int u = 0; u < D / 32; ++u) {
+            dvacc[u] = mfma32(lds_col<D>(Dt, off, u, qq, hh), pb[hh], dvacc[u]);
+            dkacc[u] = mfma32(lds_col<D>(Qt, off, u, qq, hh), dsb[hh], dkacc[u]);
           }
+      }
     }
     qt = qt_next;
     ua = ua_n;
     ub = ub_n;
     have = have_next;
-    buf ^= 1;
+  };
+  while (have) {
+    step(Parity<0>{});
+    if (!have) break;
+    step(Parity<1>{});
   }
   uint16_t* st = (uint16_t*)&smem[0][0][0];
   __syncthreads();
