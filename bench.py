@@ -44,6 +44,8 @@ def parse():
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--cpu-budget", type=float, default=20.0, help="target seconds of CPU oracle work")
     ap.add_argument("--dump-index", default="", help="write the block index of the last step to this .npz")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="first run one plain 512 MiB device-to-device copy (a known-size kernel for HBM counters)")
     return ap.parse_args()
 
 
@@ -146,6 +148,12 @@ def main():
     o = torch.empty_like(q)
     dq, dk, dv = (torch.empty_like(q) for _ in range(3))
     layer = PrismLayer(shape, par, device=dev)
+    if args.calibrate_copy:
+        src = torch.empty(512 << 20, dtype=torch.uint8, device=dev).fill_(1)
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
     stream = torch.cuda.current_stream(dev)
 
     names = ["zone_stats", "plan_shapes", "select_blocks", "attn_fwd", "attn_bwd"]

@@ -44,6 +44,7 @@ constexpr float kRescale = 8.0f;   // log2 headroom before the running max moves
 constexpr int kThreads = 256;
 
 typedef __attribute__((__vector_size__(4 * sizeof(short)))) short short4v;
+typedef __attribute__((__vector_size__(2 * sizeof(__bf16)))) __bf16 bf16x2;
 typedef __attribute__((address_space(3))) void lds_void;
 typedef __attribute__((address_space(3))) short4v lds_short4;
 
@@ -166,14 +167,42 @@ __device__ __forceinline__ void store_pair_thw(const uint16_t* st, uint16_t* __r
   }
 }
 
+// A window on an ascending block list: lane i holds entry base + i (block
+// index and its tile range, loaded together), so the iterator reads the next
+// block with a lane read instead of two dependent memory round trips, and
+// refills once per 64 blocks.
+struct ListWin {
+  const int32_t* idx;
+  int n, base, pos;
+  int vj, vs, ve;   // per lane: block index, first tile, end tile of entry base + lane
+
+  __device__ __forceinline__ void refill(const int32_t* __restrict__ bs) {
+    base = pos;
+    const int e = base + (int)(threadIdx.x & 63);
+    vj = INT_MAX;
+    vs = ve = 0;
+    if (e < n) {
+      vj = idx[e];
+      vs = bs[vj];
+      ve = bs[vj + 1];
+    }
+  }
+  // block index at the current position (INT_MAX past the end)
+  __device__ __forceinline__ int peek(const int32_t* __restrict__ bs) {
+    if (pos >= n) return INT_MAX;
+    if (pos - base >= 64) refill(bs);
+    return __builtin_amdgcn_readlane(vj, pos - base);
+  }
+  __device__ __forceinline__ int start() const { return __builtin_amdgcn_readlane(vs, pos - base); }
+  __device__ __forceinline__ int end() const { return __builtin_amdgcn_readlane(ve, pos - base); }
+};
+
 // Walks the tiles of the union of two ascending block lists (one per tile of
 // the pair), in ascending block order, with a flag per list.  Uniform across
 // the workgroup.
 struct PairIter {
-  const int32_t* la;
-  const int32_t* lb;
+  ListWin a, b;
   const int32_t* bs;
-  int ia, na, ib, nb;
   bool same, dense;
   int kt, kt_end;
   bool ua, ub;
@@ -181,16 +210,21 @@ struct PairIter {
   __device__ bool next(int& tile, bool& use_a, bool& use_b) {
     if (kt >= kt_end) {
       if (dense) return false;
-      const int ja = ia < na ? la[ia] : INT_MAX;
-      const int jb = same ? ja : (ib < nb ? lb[ib] : INT_MAX);
+      const int ja = a.peek(bs);
+      const int jb = same ? ja : b.peek(bs);
       const int j = ja < jb ? ja : jb;
       if (j == INT_MAX) return false;
       ua = ja == j;
       ub = jb == j;
-      if (ua) ++ia;
-      if (!same && ub) ++ib;
-      kt = bs[j];
-      kt_end = bs[j + 1];
+      if (ua) {
+        kt = a.start();
+        kt_end = a.end();
+        ++a.pos;
+      } else {
+        kt = b.start();
+        kt_end = b.end();
+      }
+      if (!same && ub) ++b.pos;
     }
     tile = kt++;
     use_a = ua;
@@ -211,8 +245,8 @@ __device__ __forceinline__ PairIter make_iter(const Geometry& g, int h, int pair
     it.dense = true;
     it.same = true;
     it.kt_end = (int)g.tiles;
-    it.la = it.lb = it.bs = nullptr;
-    it.ia = it.na = it.ib = it.nb = 0;
+    it.bs = nullptr;
+    it.a.n = it.b.n = 0;
     return it;
   }
   it.dense = false;
@@ -222,12 +256,15 @@ __device__ __forceinline__ PairIter make_iter(const Geometry& g, int h, int pair
   const int bb = block_of_tile(bs, nbk, 2 * pair + 1);
   const int32_t* rp = ptr + (int64_t)h * (g.tiles + 1);
   it.bs = bs;
-  it.la = idx + rp[ba];
-  it.na = rp[ba + 1] - rp[ba];
-  it.lb = idx + rp[bb];
-  it.nb = rp[bb + 1] - rp[bb];
-  it.ia = it.ib = 0;
   it.same = ba == bb;
+  it.a.idx = idx + rp[ba];
+  it.a.n = rp[ba + 1] - rp[ba];
+  it.a.pos = 0;
+  it.a.refill(bs);
+  it.b.idx = idx + rp[bb];
+  it.b.n = rp[bb + 1] - rp[bb];
+  it.b.pos = 0;
+  if (!it.same) it.b.refill(bs);
   return it;
 }
 
@@ -293,12 +330,13 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(
       const char* Vt = smem[B][1];
       floatx16 sacc[2];
 #pragma unroll
-      for (int kk = 0; kk < 2; ++kk) {
+      for (int kk = 0; kk < 2; ++kk)
 #pragma unroll
         for (int i = 0; i < 16; ++i) sacc[kk][i] = 0.0f;
 #pragma unroll
-        for (int s = 0; s < D / 16; ++s) sacc[kk] = mfma32(lds_row<D>(Kt, off, kk, s), qreg[s], sacc[kk]);
-      }
+      for (int s = 0; s < D / 16; ++s)
+#pragma unroll
+        for (int kk = 0; kk < 2; ++kk) sacc[kk] = mfma32(lds_row<D>(Kt, off, kk, s), qreg[s], sacc[kk]);
       float mloc = sacc[0][0];
 #pragma unroll
       for (int kk = 0; kk < 2; ++kk)
@@ -322,14 +360,20 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(
       for (int kk = 0; kk < 2; ++kk)
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
-          // O is normalised by the sum of the same bf16-rounded weights the PV
-          // product uses; the log-sum-exp keeps the float32 weights
           const float pv = fast_exp2(__builtin_fmaf(sacc[kk][i], sl2, -m_run));
-          const __bf16 pr = (__bf16)pv;
           lsum += pv;
-          rsum += (float)pr;
-          pb[kk * 2 + (i >> 3)][i & 7] = pr;
+          pb[kk * 2 + (i >> 3)][i & 7] = (__bf16)pv;
         }
+      // O is normalised by the sum of the same bf16-rounded weights the PV
+      // product uses (two per v_dot2); the log-sum-exp keeps the float32 weights
+      const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        rsum = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pb[v], pb[v], 0, 1), ones, rsum, false);
+        rsum = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pb[v], pb[v], 2, 3), ones, rsum, false);
+        rsum = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pb[v], pb[v], 4, 5), ones, rsum, false);
+        rsum = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pb[v], pb[v], 6, 7), ones, rsum, false);
+      }
       l_run += lsum;
       r_run += rsum;
 #pragma unroll

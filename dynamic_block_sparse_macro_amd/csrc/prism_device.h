@@ -43,12 +43,18 @@ __host__ __device__ constexpr ShapeTable make_shape_table() {
 }
 
 // Operand tiles of the attention kernels are 64 rows x D bf16, row-major, with
-// the 16-byte chunk c of row r stored at chunk position swz_chunk<D>(r, c).  The
-// XOR pattern keeps both the 16-byte row reads and the 8-byte transposing reads
-// of a wave on distinct LDS banks, and the tile can be copied to LDS verbatim.
+// the 16-byte chunk c of row r stored at chunk position swz_chunk<D>(r, c) =
+// c ^ f(r).  For D = 128 (16 chunks = all 64 banks per row) f permutes the bits
+// of r mod 16 so that (a) 16 consecutive rows get 16 different f (16-byte row
+// reads of 16 lanes hit distinct banks) and (b) the four rows read together by
+// a transposing 8-byte read differ in bits 2-3 of f (the 4 x 4 chunks two
+// 16-lane groups touch land on 16 distinct positions).  For D = 64 (a row is
+// half the banks) f has the same two properties per bank half.  The tile can
+// be copied to LDS verbatim.
 template <int D>
 __host__ __device__ __forceinline__ constexpr int swz_chunk(int r, int c) {
-  return D == 128 ? (c ^ (((r & 7) << 1) | ((r >> 3) & 1))) : (c ^ (r & 7));
+  return D == 128 ? (c ^ (((r & 3) << 2) | (((r >> 2) & 1) << 1) | ((r >> 3) & 1)))
+                  : (c ^ ((((r >> 1) & 1) << 2) | (((r >> 2) & 1) << 1) | ((r >> 3) & 1)));
 }
 
 __device__ __forceinline__ float bf16_to_f32(uint16_t b) { return __uint_as_float(((uint32_t)b) << 16); }

@@ -144,8 +144,9 @@ int prism_plan_shapes(const prism_problem *prob, const prism_params *par, const 
  *             rows in block order, grouped in tiles of 64 rows; inside a tile
  *             row r is contiguous (D values) but its 16-byte chunk c (values
  *             8c .. 8c+7) is stored at chunk position c ^ f(r), with
- *             f(r) = ((r & 7) << 1) | ((r >> 3) & 1) for D = 128 and
- *             f(r) = r & 7 for D = 64.  Element (head, p, c) is therefore at
+ *             f(r) = ((r&3)<<2) | (((r>>2)&1)<<1) | ((r>>3)&1) for D = 128 and
+ *             f(r) = (((r>>1)&1)<<2) | (((r>>2)&1)<<1) | ((r>>3)&1) for D = 64.
+ *             Element (head, p, c) is therefore at
  *             (head * N + p) * D + 8 * ((c / 8) ^ f(p % 64)) + c % 8.
  * row_ptr     int32 [heads][N/64 + 1] (out): CSR row pointers of the
  *             query-major block index, offsets into col_idx counted over

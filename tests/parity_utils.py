@@ -125,13 +125,18 @@ def check_partition(gidx: dict, perm: np.ndarray, blk_start: np.ndarray):
 
 def unswizzle_tiles(stored: np.ndarray, D: int) -> np.ndarray:
     """Operand layout -> plain rows.  Each 64-row tile is row-major with the
-    16-byte chunk c of row r stored at chunk position c ^ f(r), f(r) =
-    ((r & 7) << 1) | ((r >> 3) & 1) for D = 128 and r & 7 for D = 64."""
+    16-byte chunk c of row r stored at chunk position c ^ f(r), with
+    f(r) = ((r & 3) << 2) | (((r >> 2) & 1) << 1) | ((r >> 3) & 1) for D = 128
+    and f(r) = (((r >> 1) & 1) << 2) | (((r >> 2) & 1) << 1) | ((r >> 3) & 1)
+    for D = 64."""
     n = stored.shape[0]
     ch = D // 8
     t = stored.reshape(n // 64, 64, ch, 8)
     r = np.arange(64)
-    f = (((r & 7) << 1) | ((r >> 3) & 1)) if D == 128 else (r & 7)
+    if D == 128:
+        f = ((r & 3) << 2) | (((r >> 2) & 1) << 1) | ((r >> 3) & 1)
+    else:
+        f = (((r >> 1) & 1) << 2) | (((r >> 2) & 1) << 1) | ((r >> 3) & 1)
     pos = np.arange(ch)[None, :] ^ f[:, None]            # [64][ch]: stored position of logical chunk c
     return t[:, r[:, None], pos, :].reshape(n, D)
 
