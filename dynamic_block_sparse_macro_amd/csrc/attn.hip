@@ -406,7 +406,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(
 }
 
 // ---------------------------------------------------------------------------
-// backward pre-pass: dO into the operand layout, delta = rowsum(dO * O),
+// backward pre-pass: dO into the operand layout, -delta = -rowsum(dO * O),
 // lse2 = lse * log2(e)
 // ---------------------------------------------------------------------------
 template <int D>
@@ -437,7 +437,7 @@ __global__ __launch_bounds__(256) void bwd_pre_kernel(Geometry g, const uint16_t
 #pragma unroll
     for (int off2 = CH / 2; off2 > 0; off2 >>= 1) acc += __shfl_xor(acc, off2, CH);
     if (k == 0) {
-      delta[p0 + r] = acc;
+      delta[p0 + r] = -acc;   // stored negated: it seeds the dP accumulators
       lse2[p0 + r] = lse[p0 + r] * kLog2e;
     }
   }
@@ -478,7 +478,12 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bwd_dq_kernel(
     }
   }
   const float l2 = lse2[hN + qt * kTile + rloc];
-  const float dlt = delta[hN + qt * kTile + rloc];
+  floatx16 ndelta;   // -delta of this lane's query row: the dP accumulators start here
+  {
+    const float nd = delta[hN + qt * kTile + rloc];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) ndelta[i] = nd;
+  }
   floatx16 dqacc[D / 32];
 #pragma unroll
   for (int u = 0; u < D / 32; ++u)
@@ -507,19 +512,19 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bwd_dq_kernel(
       const char* Vt = smem[B][1];
 #pragma unroll
       for (int kk = 0; kk < 2; ++kk) {
-        floatx16 sacc, pacc;
+        floatx16 sacc, pacc = ndelta;
 #pragma unroll
-        for (int i = 0; i < 16; ++i) sacc[i] = pacc[i] = 0.0f;
+        for (int i = 0; i < 16; ++i) sacc[i] = 0.0f;
 #pragma unroll
         for (int s = 0; s < D / 16; ++s) {
           sacc = mfma32(lds_row<D>(Kt, off, kk, s), qreg[s], sacc);
-          pacc = mfma32(lds_row<D>(Vt, off, kk, s), dreg[s], pacc);
+          pacc = mfma32(lds_row<D>(Vt, off, kk, s), dreg[s], pacc);   // dP - delta
         }
         bf16x8 dsb[2];
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
           const float pv = fast_exp2(__builtin_fmaf(sacc[i], sl2, -l2));
-          dsb[i >> 3][i & 7] = (__bf16)(pv * (pacc[i] - dlt));
+          dsb[i >> 3][i & 7] = (__bf16)(pv * pacc[i]);
         }
 #pragma unroll
         for (int hh = 0; hh < 2; ++hh)
@@ -607,35 +612,57 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bwd_dkdv_kernel(
       const char* Dt = smem[B][1];
 #pragma unroll
       for (int qq = 0; qq < 2; ++qq) {
-        floatx16 sacc, pacc;
-#pragma unroll
-        for (int i = 0; i < 16; ++i) sacc[i] = pacc[i] = 0.0f;
+        // all LDS operands of this half first, so their latency overlaps the MFMAs
+        bf16x8 qa[D / 16], da[D / 16];
 #pragma unroll
         for (int s = 0; s < D / 16; ++s) {
-          sacc = mfma32(lds_row<D>(Qt, off, qq, s), kreg[s], sacc);
-          pacc = mfma32(lds_row<D>(Dt, off, qq, s), vreg[s], pacc);
+          qa[s] = lds_row<D>(Qt, off, qq, s);
+          da[s] = lds_row<D>(Dt, off, qq, s);
         }
+        floatx16 sacc, pacc;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          // dP starts at -delta of each query row (rows 32 qq + 8 j + 4 g + e)
+          const float4 d4 = *(const float4*)(&svec[B][1][32 * qq + 8 * j + 4 * g32]);
+          pacc[4 * j] = d4.x;
+          pacc[4 * j + 1] = d4.y;
+          pacc[4 * j + 2] = d4.z;
+          pacc[4 * j + 3] = d4.w;
+        }
+#pragma unroll
+        for (int i = 0; i < 16; ++i) sacc[i] = 0.0f;
+#pragma unroll
+        for (int s = 0; s < D / 16; ++s) {
+          sacc = mfma32(qa[s], kreg[s], sacc);
+          pacc = mfma32(da[s], vreg[s], pacc);   // dP - delta
+        }
+        bf16x8 dta[2][D / 32], qta[2][D / 32];
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh)
+#pragma unroll
+          for (int u = 0; u < D / 32; ++u) {
+            dta[hh][u] = lds_col<D>(Dt, off, u, qq, hh);
+            qta[hh][u] = lds_col<D>(Qt, off, u, qq, hh);
+          }
         bf16x8 pb[2], dsb[2];
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-          const int q0 = 32 * qq + 8 * j + 4 * g32;
-          const float4 l4 = *(const float4*)(&svec[B][0][q0]);
-          const float4 d4 = *(const float4*)(&svec[B][1][q0]);
-          const float lv[4] = {l4.x, l4.y, l4.z, l4.w}, dvv[4] = {d4.x, d4.y, d4.z, d4.w};
+          const float4 l4 = *(const float4*)(&svec[B][0][32 * qq + 8 * j + 4 * g32]);
+          const float lv[4] = {l4.x, l4.y, l4.z, l4.w};
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
             const int i = 4 * j + e;
             const float pv = fast_exp2(__builtin_fmaf(sacc[i], sl2, -lv[e]));
             pb[i >> 3][i & 7] = (__bf16)pv;
-            dsb[i >> 3][i & 7] = (__bf16)(pv * (pacc[i] - dvv[e]));
+            dsb[i >> 3][i & 7] = (__bf16)(pv * pacc[i]);
           }
         }
 #pragma unroll
         for (int hh = 0; hh < 2; ++hh)
 #pragma unroll
           for (int u = 0; u < D / 32; ++u) {
-            dvacc[u] = mfma32(lds_col<D>(Dt, off, u, qq, hh), pb[hh], dvacc[u]);
-            dkacc[u] = mfma32(lds_col<D>(Qt, off, u, qq, hh), dsb[hh], dkacc[u]);
+            dvacc[u] = mfma32(dta[hh][u], pb[hh], dvacc[u]);
+            dkacc[u] = mfma32(qta[hh][u], dsb[hh], dkacc[u]);
           }
       }
     }
