@@ -337,6 +337,14 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(
       for (int s = 0; s < D / 16; ++s)
 #pragma unroll
         for (int kk = 0; kk < 2; ++kk) sacc[kk] = mfma32(lds_row<D>(Kt, off, kk, s), qreg[s], sacc[kk]);
+      // V^T operands do not depend on P: issue their LDS reads before the softmax
+      bf16x8 va[2][2][D / 32];
+#pragma unroll
+      for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh)
+#pragma unroll
+          for (int u = 0; u < D / 32; ++u) va[kk][hh][u] = lds_col<D>(Vt, off, u, kk, hh);
       float mloc = sacc[0][0];
 #pragma unroll
       for (int kk = 0; kk < 2; ++kk)
@@ -381,8 +389,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(
 #pragma unroll
         for (int hh = 0; hh < 2; ++hh)
 #pragma unroll
-          for (int u = 0; u < D / 32; ++u)
-            oacc[u] = mfma32(lds_col<D>(Vt, off, u, kk, hh), pb[kk * 2 + hh], oacc[u]);
+          for (int u = 0; u < D / 32; ++u) oacc[u] = mfma32(va[kk][hh][u], pb[kk * 2 + hh], oacc[u]);
     }
     kt = kt_next;
     ua = ua_n;
@@ -520,6 +527,11 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bwd_dq_kernel(
           sacc = mfma32(lds_row<D>(Kt, off, kk, s), qreg[s], sacc);
           pacc = mfma32(lds_row<D>(Vt, off, kk, s), dreg[s], pacc);   // dP - delta
         }
+        bf16x8 ka[2][D / 32];   // K^T operands, read before the dS arithmetic
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh)
+#pragma unroll
+          for (int u = 0; u < D / 32; ++u) ka[hh][u] = lds_col<D>(Kt, off, u, kk, hh);
         bf16x8 dsb[2];
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
@@ -529,7 +541,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bwd_dq_kernel(
 #pragma unroll
         for (int hh = 0; hh < 2; ++hh)
 #pragma unroll
-          for (int u = 0; u < D / 32; ++u) dqacc[u] = mfma32(lds_col<D>(Kt, off, u, kk, hh), dsb[hh], dqacc[u]);
+          for (int u = 0; u < D / 32; ++u) dqacc[u] = mfma32(ka[hh][u], dsb[hh], dqacc[u]);
       }
     }
     kt = kt_next;
