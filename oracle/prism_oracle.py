@@ -74,6 +74,8 @@ __all__ = [
     "masked_attention_thw", "token_block_map",
     "Params", "run_pipeline", "row_tie_affected", "row_is_valid_alternative",
     "attention_flops", "selected_pairs",
+    "VARIANT_FIXED_SHAPE", "VARIANT_TOPK_ONLY", "VARIANT_TOPP_ONLY", "VARIANT_VISUAL_ONLY", "VARIANT_AUDIO_ONLY",
+    "VARIANT_RHO_MAX_AUDIO",
 ]
 
 ZONE = 8                      # Z_T = Z_H = Z_W = 8 [pt/IC]
@@ -81,6 +83,19 @@ TOL_SCORE = 1e-6              # block-score ties (absolute)
 TOL_MASS = 1e-9               # cumulative-probability ties at the Top-p cut
 TOL_DIST = 1e-6               # shape-distance ties
 TOL_RHO = 1e-6                # density ties at tau_128 / tau_256
+
+
+# Variant switches (bit flags; 0 = the method as the pages describe it).  The
+# pages' ablations compare against fixed block shapes, Top-k-only and
+# Top-p-only selection, and guidance from the video or the audio signal alone
+# (sd114.wiki post, 测试结果 items 2-3); RHO_MAX_AUDIO lets the audio coupling
+# raise the density (an alternative reading of "information density").
+VARIANT_FIXED_SHAPE = 1
+VARIANT_TOPK_ONLY = 2
+VARIANT_TOPP_ONLY = 4
+VARIANT_VISUAL_ONLY = 8
+VARIANT_AUDIO_ONLY = 16
+VARIANT_RHO_MAX_AUDIO = 32
 
 
 @dataclass(frozen=True)
@@ -93,6 +108,8 @@ class Params:
     top_p: float = 0.9
     density_cap: float = 1.0
     scale: float = 0.0            # 0 -> 1 / sqrt(head_dim)
+    variant: int = 0              # VARIANT_* bits
+    fixed_shape: int = 0          # candidate index used with VARIANT_FIXED_SHAPE
 
     def score_scale(self, head_dim: int) -> float:
         return self.scale if self.scale > 0 else 1.0 / math.sqrt(head_dim)
@@ -208,13 +225,24 @@ def information_density(sv2: np.ndarray) -> np.ndarray:
     return np.where(mx > 0, E / np.where(mx > 0, mx, 1.0), 0.0)
 
 
-def zone_statistics(v: np.ndarray, a: np.ndarray | None, T: int, H: int, W: int, eps: float = 1e-6) -> dict:
-    """Everything the zone-statistics step produces, per head."""
+def zone_statistics(v: np.ndarray, a: np.ndarray | None, T: int, H: int, W: int, eps: float = 1e-6,
+                    variant: int = 0) -> dict:
+    """Everything the zone-statistics step produces, per head.  With
+    VARIANT_VISUAL_ONLY the audio term is dropped (g = r + eps), with
+    VARIANT_AUDIO_ONLY the video ratio (g = a-bar v-hat + eps); with
+    VARIANT_RHO_MAX_AUDIO the density is max(rho, a-bar)."""
     sv2 = video_variation(v, T, H, W)
     r = _normalise_over_axes(sv2)                # r_v,d(m) [pt/M1]
     abar, vhat, mu_a, sa2 = audio_terms(a, T, H, W)
-    g = composite_indicator(r, abar, vhat, eps)
+    if variant & VARIANT_VISUAL_ONLY:
+        g = r + eps
+    elif variant & VARIANT_AUDIO_ONLY:
+        g = np.broadcast_to(abar[:, None] * vhat, r.shape) + eps
+    else:
+        g = composite_indicator(r, abar, vhat, eps)
     rho = information_density(sv2)
+    if variant & VARIANT_RHO_MAX_AUDIO:
+        rho = np.maximum(rho, abar[None, :])
     return dict(sv2=sv2, r=r, E=sv2.sum(-1), abar=abar, vhat=vhat, mu_a=mu_a, sa2=sa2, g=g, rho=rho)
 
 
@@ -385,11 +413,13 @@ def _sorted_order(s_row: np.ndarray) -> np.ndarray:
 
 
 def select_row(s_row: np.ndarray, P_row: np.ndarray, sizes: np.ndarray, top_k: int, top_p: float,
-               density_cap: float, N: int) -> dict:
+               density_cap: float, N: int, variant: int = 0) -> dict:
     """S_i = Top-k(P_i, k) U Top-p(P_i, p) ([pt/M3]; R12-R14).
 
     Both parts are prefixes of the same descending order, so the union is
-    the longer prefix; the optional density cap limits the Top-p extension."""
+    the longer prefix; the optional density cap limits the Top-p extension.
+    VARIANT_TOPK_ONLY keeps Top-k alone; VARIANT_TOPP_ONLY keeps the (capped)
+    Top-p prefix alone, at least one block."""
     nb = s_row.size
     order = _sorted_order(s_row)
     C = np.cumsum(P_row[order])
@@ -405,8 +435,13 @@ def select_row(s_row: np.ndarray, P_row: np.ndarray, sizes: np.ndarray, top_k: i
         U = math.floor(density_cap * N)
         tok = np.cumsum(sizes[order])
         n_cap = int(np.searchsorted(tok, U, side="right"))
-    L = max(n_k, min(n_p, n_cap))
-    return dict(order=order, C=C, n_p=n_p, n_k=n_k, n_cap=n_cap, L=L, cols=np.sort(order[:L]))
+    if variant & VARIANT_TOPK_ONLY:
+        L = n_k
+    elif variant & VARIANT_TOPP_ONLY:
+        L = max(1, min(n_p, n_cap))
+    else:
+        L = max(n_k, min(n_p, n_cap))
+    return dict(order=order, C=C, n_p=n_p, n_k=n_k, n_cap=n_cap, L=L, cols=np.sort(order[:L]), variant=variant)
 
 
 def row_tie_affected(s_row: np.ndarray, sel: dict, top_p: float, capped: bool,
@@ -421,12 +456,13 @@ def row_tie_affected(s_row: np.ndarray, sel: dict, top_p: float, capped: bool,
 
     if gap(L) <= tol_s:
         return True
-    if top_p < 1.0 and L == sel["n_p"] and L > sel["n_k"]:
+    uses_p = not (sel.get("variant", 0) & VARIANT_TOPK_ONLY)
+    if uses_p and top_p < 1.0 and L == sel["n_p"]:
         C = sel["C"]
         n_p = sel["n_p"]
         if abs(C[n_p - 1] - top_p) <= tol_m or (n_p >= 2 and abs(C[n_p - 2] - top_p) <= tol_m):
             return True
-    if capped and L == sel["n_cap"] and L > sel["n_k"]:
+    if uses_p and capped and L == sel["n_cap"]:
         if gap(sel["n_cap"] + 1) <= tol_s or gap(sel["n_cap"]) <= tol_s:
             return True
     return False
@@ -434,11 +470,13 @@ def row_tie_affected(s_row: np.ndarray, sel: dict, top_p: float, capped: bool,
 
 def row_is_valid_alternative(s_row: np.ndarray, cols: np.ndarray, sel: dict, tol_s: float = TOL_SCORE) -> bool:
     """For a tie-affected row: is `cols` a selection some rounding of the scores
-    could produce?  It must keep the Top-k floor, be a prefix of the score
+    could produce?  It must keep the Top-k floor (one block for Top-p
+    alone), be a prefix of the score
     order up to the tie tolerance, and have a length within two of the
     oracle's."""
     cols = np.asarray(cols)
-    if cols.size < sel["n_k"] or abs(cols.size - sel["L"]) > 2:
+    floor = 1 if sel.get("variant", 0) & VARIANT_TOPP_ONLY else sel["n_k"]
+    if cols.size < floor or abs(cols.size - sel["L"]) > 2:
         return False
     if np.unique(cols).size != cols.size or (np.diff(cols) <= 0).any():
         return False
@@ -465,7 +503,7 @@ def select_blocks(qp: np.ndarray, kp: np.ndarray, blk_start: np.ndarray, params:
     for i in rows:
         s_row = block_scores(qbar[i:i + 1], kbar, scale)[0]
         P_row = block_probabilities(s_row)
-        sel = select_row(s_row, P_row, sizes, params.top_k, params.top_p, params.density_cap, N)
+        sel = select_row(s_row, P_row, sizes, params.top_k, params.top_p, params.density_cap, N, params.variant)
         sel["s"] = s_row
         sel["tie"] = row_tie_affected(s_row, sel, params.top_p, capped)
         out_rows[int(i)] = sel
@@ -606,7 +644,9 @@ def run_pipeline(q, k, v, a, T, H, W, params: Params, do=None, attention: bool =
     """Run every step for all heads.  q, k, v, do: [heads][N][D] (bf16 values
     as float32/float64), a: [N] or None.  Returns per-step results."""
     heads, N, D = q.shape
-    zs = zone_statistics(v, a, T, H, W, params.eps)
+    zs = zone_statistics(v, a, T, H, W, params.eps, params.variant)
+    if params.variant & VARIANT_FIXED_SHAPE:
+        forced_shape = np.full(zs["rho"].shape, params.fixed_shape, np.int64)
     plan = plan_shapes(zs["g"], zs["rho"], params.tau128, params.tau256, forced_shape)
     scale = params.score_scale(D)
     res = dict(zone=zs, plan=plan, heads=[])

@@ -32,18 +32,43 @@ def _oracle_head(wl, plan, h, op):
 
 @pytest.mark.parametrize("name", CASES)
 def test_pipeline_parity(name):
+    _pipeline_parity(generate(name), {})
+
+
+# (workload, variant switches, fixed shape index): the ablation baselines
+VARIANTS = [
+    ("par_small", O.VARIANT_FIXED_SHAPE, 7),
+    ("par_d64", O.VARIANT_FIXED_SHAPE, 0),
+    ("par_cap", O.VARIANT_TOPK_ONLY, 0),
+    ("par_cap", O.VARIANT_TOPP_ONLY, 0),
+    ("par_small", O.VARIANT_VISUAL_ONLY, 0),
+    ("par_small", O.VARIANT_AUDIO_ONLY, 0),
+    ("par_small", O.VARIANT_RHO_MAX_AUDIO, 0),
+    ("par_d64", O.VARIANT_VISUAL_ONLY | O.VARIANT_TOPP_ONLY | O.VARIANT_RHO_MAX_AUDIO, 0),
+]
+
+
+@pytest.mark.parametrize("name,variant,fixed", VARIANTS)
+def test_variant_parity(name, variant, fixed):
+    _pipeline_parity(generate(name), dict(variant=variant, fixed_shape=fixed))
+
+
+def _pipeline_parity(wl, over):
     import torch
-    wl = generate(name)
+    from parity_utils import binding_params
     c = wl.cfg
-    op = oracle_params(c)
-    log("case", name, "N", c.N, "heads", c.heads, "D", c.head_dim)
-    run = GpuRun(wl)
+    op = oracle_params(c, **over)
+    log("case", c.name, "N", c.N, "heads", c.heads, "D", c.head_dim, "variant", op.variant, "fixed", op.fixed_shape)
+    run = GpuRun(wl, params=binding_params(c, **over))
     gpu = run.host()
     log("gpu done, nnz", run.nnz)
 
-    zs = O.zone_statistics(wl.f32("v"), wl.a, c.T, c.H, c.W, op.eps)
+    zs = O.zone_statistics(wl.f32("v"), wl.a, c.T, c.H, c.W, op.eps, op.variant)
     check_zone_stats(gpu, zs)
-    plan = O.plan_shapes(zs["g"], zs["rho"], op.tau128, op.tau256)
+    fixed = None
+    if op.variant & O.VARIANT_FIXED_SHAPE:
+        fixed = np.full(zs["rho"].shape, op.fixed_shape, np.int64)
+    plan = O.plan_shapes(zs["g"], zs["rho"], op.tau128, op.tau256, forced_shape=fixed)
     forced, zone_ties = reconcile_shapes(gpu["shape_id"], zs, plan, op)
     if zone_ties:
         plan = O.plan_shapes(zs["g"], zs["rho"], op.tau128, op.tau256, forced_shape=forced)
