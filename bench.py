@@ -44,6 +44,8 @@ def parse():
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--cpu-budget", type=float, default=20.0, help="target seconds of CPU oracle work")
     ap.add_argument("--dump-index", default="", help="write the block index of the last step to this .npz")
+    ap.add_argument("--a2v-channels", type=int, default=0,
+                    help="channels of the A2V producer timing (default heads * head_dim)")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="first run one plain 512 MiB device-to-device copy (a known-size kernel for HBM counters)")
     return ap.parse_args()
@@ -237,6 +239,30 @@ def main():
                      tflops=round(fd / ((dfwd + dbwd) * 1e-3) / 1e12, 1))
         log("dense", dense)
 
+    # audio-to-video norm producer (upstream of the zone statistics, not part
+    # of the timed step): HBM-bound read of h-hat
+    from dynamic_block_sparse_macro_amd.pipeline import a2v_norms
+    from workload import a2v_output
+    ch = args.a2v_channels or heads * D
+    hh = torch.from_numpy(a2v_output(wl, ch).view(np.int16)).to(dev).view(torch.bfloat16)
+    an = torch.empty(cfg.N, dtype=torch.float32, device=dev)
+    a2v_norms(hh, an)
+    e = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    reps = 20
+    torch.cuda.synchronize()
+    e[0].record(stream)
+    for _ in range(reps):
+        a2v_norms(hh, an)
+    e[1].record(stream)
+    torch.cuda.synchronize()
+    a2v_ms = e[0].elapsed_time(e[1]) / reps
+    a2v_bytes = cfg.N * (2 * ch + 4)
+    producer = dict(kernel="a2v_norm_kernel", channels=ch, ms=round(a2v_ms, 4), bytes=a2v_bytes,
+                    gbps=round(a2v_bytes / (a2v_ms * 1e-3) / 1e9, 1),
+                    frac_hbm=round(a2v_bytes / (a2v_ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4))
+    log("a2v producer", producer)
+    del hh
+
     cpu = None
     if not args.no_cpu:
         import oracle as O
@@ -278,6 +304,7 @@ def main():
         "dense_baseline": dense,
         "speedup_vs_dense": (round(dense["ms_per_head"] / (ms_step / heads), 2) if dense else None),
         "cpu_baseline": cpu,
+        "a2v_producer": producer,
         "wall_s_timed": round(wall, 3),
     }
     print(json.dumps(line), flush=True)

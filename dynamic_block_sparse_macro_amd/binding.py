@@ -32,7 +32,7 @@ VARIANT_AUDIO_ONLY = 16
 VARIANT_RHO_MAX_AUDIO = 32
 
 ENTRY_POINTS = ("prism_zone_stats", "prism_plan_shapes", "prism_select_blocks", "prism_attn_fwd",
-                "prism_attn_bwd", "prism_dense_attn_fwd", "prism_dense_attn_bwd", "prism_strerror")
+                "prism_attn_bwd", "prism_dense_attn_fwd", "prism_dense_attn_bwd", "prism_a2v_norms", "prism_strerror")
 
 
 class PrismError(RuntimeError):
@@ -88,6 +88,7 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         "prism_attn_bwd": [pp, pr] + [_vp] * 17 + [_P(ctypes.c_size_t), _vp],
         "prism_dense_attn_fwd": [pp, pr, _vp, _vp, _vp, _vp, _vp, _vp, _P(ctypes.c_size_t), _vp],
         "prism_dense_attn_bwd": [pp, pr] + [_vp] * 10 + [_P(ctypes.c_size_t), _vp],
+        "prism_a2v_norms": [_vp, ctypes.c_int64, ctypes.c_int32, ctypes.c_int64, _vp, _vp],
     }
     for name, args in sig.items():
         f = getattr(lib, name)
@@ -183,3 +184,9 @@ def prism_dense_attn_bwd(prob, par, q, k, v, o, dout, lse, dq, dk, dv, ws, ws_by
                                              _ptr(o), _ptr(dout), _ptr(lse), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(ws),
                                              _ref(ws_bytes), _stream(stream))
     return _check("prism_dense_attn_bwd", st) if check else st
+
+
+def prism_a2v_norms(h_hat, n_tokens, channels, token_stride, a, stream=None, check=True):
+    st = load_library().prism_a2v_norms(_ptr(h_hat), int(n_tokens), int(channels), int(token_stride), _ptr(a),
+                                        _stream(stream))
+    return _check("prism_a2v_norms", st) if check else st

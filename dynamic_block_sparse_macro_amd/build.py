@@ -32,7 +32,7 @@ PER_FILE = {
     "zone_plan.hip": ["-ffp-contract=off"],
     "select.hip": ["-ffp-contract=off"],
 }
-SOURCES = ["api.hip", "zone_plan.hip", "select.hip", "attn.hip"]
+SOURCES = ["api.hip", "zone_plan.hip", "select.hip", "attn.hip", "a2v.hip"]
 
 
 def hipcc() -> str:

@@ -98,6 +98,15 @@ const char* prism_strerror(int status) {
   }
 }
 
+int prism_a2v_norms(const prism_bf16* h_hat, int64_t n_tokens, int32_t channels, int64_t token_stride, float* a,
+                    prism_stream stream) {
+  if (!h_hat || !a || ((uintptr_t)h_hat & 15)) return PRISM_EINVAL;
+  if (n_tokens < 0 || n_tokens > INT32_MAX || channels <= 0 || channels % 8) return PRISM_EINVAL;
+  if (token_stride < channels || token_stride % 8) return PRISM_EINVAL;
+  HIPCALL(prism::launch_a2v_norms(h_hat, n_tokens, channels, token_stride, a, (hipStream_t)stream));
+  return PRISM_OK;
+}
+
 int prism_zone_stats(const prism_problem* prob, const prism_params* par, const prism_bf16* v, const float* a,
                      double* zstats, double* g, double* rho, prism_stream stream) {
   Geometry geo;

@@ -54,4 +54,8 @@ hipError_t launch_attn_bwd(const Geometry& g, float scale, const uint16_t* qp, c
                            const int32_t* row_ptr, const int32_t* col_idx, const int32_t* t_row_ptr,
                            const int32_t* t_col_idx, uint16_t* dq, uint16_t* dk, uint16_t* dv, hipStream_t s);
 
+// ---- audio-to-video norm producer (a2v.hip) ----
+hipError_t launch_a2v_norms(const uint16_t* h_hat, int64_t n, int channels, int64_t stride, float* a,
+                            hipStream_t s);
+
 }  // namespace prism

@@ -36,6 +36,19 @@ class LayerShape:
         return self.N // 64
 
 
+def a2v_norms(h_hat: torch.Tensor, out: torch.Tensor | None = None) -> torch.Tensor:
+    """a[n] = |h_hat[n]|_2 (float32) for a bf16 [N][C] tensor whose rows are
+    THW tokens: the audio guidance map the next layer's zone statistics
+    read.  Runs prism_a2v_norms on the current stream."""
+    if h_hat.dtype != torch.bfloat16 or h_hat.dim() != 2 or h_hat.stride(1) != 1:
+        raise ValueError("h_hat must be a bf16 [N][C] tensor with unit channel stride")
+    n, c = h_hat.shape
+    if out is None:
+        out = torch.empty(n, dtype=torch.float32, device=h_hat.device)
+    B.prism_a2v_norms(h_hat, n, c, h_hat.stride(0), out, stream=torch.cuda.current_stream())
+    return out
+
+
 class PrismLayer:
     def __init__(self, shape: LayerShape, params: B.Params, device="cuda", col_cap: int | None = None,
                  head_stride: int | None = None, token_stride: int | None = None):

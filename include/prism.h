@@ -220,6 +220,24 @@ int prism_dense_attn_bwd(const prism_problem *prob, const prism_params *par, con
                          const float *lse, prism_bf16 *dq, prism_bf16 *dk, prism_bf16 *dv, void *ws,
                          size_t *ws_bytes, prism_stream stream);
 
+/*
+ * prism_a2v_norms -- the audio guidance map a_n = |h-hat_n|_2 of every video
+ * token ([pt/M1], second paragraph: norms of the audio-to-video
+ * cross-attention output, cached for the next layer's prism_zone_stats).
+ *
+ * h_hat        bf16 [n_tokens] x [channels] (row n at h_hat + n * token_stride),
+ *              THW token order; 16-byte aligned.
+ * n_tokens     rows, 0 <= n_tokens <= INT32_MAX (0 launches nothing).
+ * channels     values per row, a positive multiple of 8.
+ * token_stride element stride between rows, a multiple of 8, >= channels.
+ * a            float [n_tokens] (out): the norm, from a float64 sum of the
+ *              (exact) squares, rounded once to float32.
+ * Returns PRISM_EINVAL for a NULL or misaligned pointer or a bad size; reads
+ * h_hat once (HBM-bound).  Asynchronous on `stream`.
+ */
+int prism_a2v_norms(const prism_bf16 *h_hat, int64_t n_tokens, int32_t channels, int64_t token_stride, float *a,
+                    prism_stream stream);
+
 /* Human-readable text of a status code (static storage). */
 const char *prism_strerror(int status);
 

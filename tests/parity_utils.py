@@ -175,6 +175,24 @@ def check_transpose(gidx: dict):
     np.testing.assert_array_equal(gidx["t_col_idx"], tc)
 
 
+def check_f32_rounding(gpu: np.ndarray, ref: np.ndarray, rel_tie: float = 1e-12) -> int:
+    """gpu (float32) must be ref (float64) rounded to nearest; where ref lies
+    within rel_tie of the midpoint between two float32 values either
+    neighbour is accepted.  Returns the number of such ties taken the other
+    way."""
+    gpu = np.asarray(gpu, np.float32)
+    near = ref.astype(np.float32)
+    bad = gpu != near
+    if not bad.any():
+        return 0
+    g, r, n = gpu[bad], ref[bad], near[bad]
+    up, down = np.nextafter(n, np.float32(np.inf)), np.nextafter(n, np.float32(-np.inf))
+    assert ((g == up) | (g == down)).all(), "GPU value more than one float32 step from the reference"
+    mid = (g.astype(np.float64) + n.astype(np.float64)) / 2
+    assert (np.abs(r - mid) <= rel_tie * np.abs(r)).all(), "GPU value is not a correct rounding"
+    return int(bad.sum())
+
+
 def fwd_errors(o_gpu: np.ndarray, o_ref: np.ndarray) -> tuple[float, float]:
     d = np.abs(o_gpu.astype(np.float64) - o_ref)
     return float(d.max()), float(d.mean())

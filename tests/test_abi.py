@@ -106,3 +106,15 @@ def test_workspace_queries(lib):
     assert nd.value >= 3 * 2 * 4096 * 128 * 2
     assert B.prism_select_blocks(prob, par, *([16] * 11), -1, 16, 16, 16, 16, n, check=False) == B.PRISM_EINVAL
     assert B.prism_attn_bwd(prob, par, *([16] * 17), None, check=False) == B.PRISM_EINVAL
+
+
+def test_a2v_norms_validation(lib):
+    """Bad sizes, strides and pointers are rejected before any launch."""
+    ok = dict(h_hat=256, n_tokens=100, channels=64, token_stride=64, a=256)
+    for over in (dict(h_hat=None), dict(a=None), dict(h_hat=264), dict(channels=0), dict(channels=60),
+                 dict(token_stride=32), dict(token_stride=68), dict(n_tokens=-1), dict(n_tokens=2 ** 31)):
+        kw = dict(ok)
+        kw.update(over)
+        assert B.prism_a2v_norms(check=False, **kw) == B.PRISM_EINVAL, over
+    # no rows: nothing to do, no launch
+    assert B.prism_a2v_norms(256, 0, 64, 64, 256, check=False) == B.PRISM_OK

@@ -101,6 +101,20 @@ def test_audio_terms_closed_forms():
     np.testing.assert_array_equal(abar1, 0.0)
 
 
+def test_a2v_norm_integer_cases():
+    """Rows that are Pythagorean quadruples (and their permutations, signs
+    and zero padding) have integer norms; a zero row has norm 0."""
+    rows = [(1, 2, 2, 3), (2, 3, 6, 7), (1, 4, 8, 9), (2, 6, 9, 11), (4, 4, 7, 9), (6, 6, 7, 11)]
+    h = np.zeros((len(rows) + 1, 64))
+    rng = np.random.default_rng(0)
+    for i, (x, y, z, _) in enumerate(rows):
+        pos = rng.choice(64, 3, replace=False)
+        h[i, pos] = np.array([x, -y, z]) * rng.choice([-1, 1])
+    got = O.a2v_norms(h)
+    np.testing.assert_array_equal(got[:-1], [r[3] for r in rows])
+    assert got[-1] == 0.0
+
+
 def test_a2v_norm_matches_generator():
     from workload import generate
     w = generate("tiny")

@@ -7,4 +7,5 @@ directional content variation, compact sounding regions), and rounds them to
 bfloat16.
 """
 
-from .generator import CONFIGS, Workload, WorkloadConfig, bf16_bits_to_f32, bf16_round, generate  # noqa: F401
+from .generator import (CONFIGS, Workload, WorkloadConfig, a2v_output, bf16_bits_to_f32, bf16_round,  # noqa: F401
+                        generate)

@@ -220,3 +220,22 @@ def generate(cfg: WorkloadConfig | str, *, keep_fp32: bool = False) -> Workload:
     if keep_fp32:
         wl.extras.update(q32=q, k32=k, v32=v, do32=do)
     return wl
+
+
+def a2v_output(wl: Workload, channels: int, token_stride: int | None = None) -> np.ndarray:
+    """Synthetic audio-to-video cross-attention output h-hat [N][channels]
+    (bf16 bit patterns, rows padded to token_stride values) for a workload
+    of any size: h_n = a_n * z_n / sqrt(channels) with z_n ~ N(0, I) from a
+    stream of its own (seed + 7919 * channels), so the workload's other draws
+    do not change and |h_n| is close to a_n.  The padding holds bf16 NaN,
+    which no reader may touch."""
+    N = wl.cfg.N
+    stride = channels if token_stride is None else token_stride
+    rng = np.random.Generator(np.random.PCG64(wl.cfg.seed + 7919 * channels))
+    out = np.full((N, stride), 0x7FC0, np.uint16)
+    step = 1 << 16
+    for s0 in range(0, N, step):
+        z = rng.standard_normal((min(step, N - s0), channels), dtype=np.float32)
+        z *= (wl.a[s0:s0 + z.shape[0]] / np.float32(np.sqrt(channels)))[:, None]
+        out[s0:s0 + z.shape[0], :channels] = bf16_round(z)
+    return out
