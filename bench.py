@@ -44,6 +44,7 @@ def parse():
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--cpu-budget", type=float, default=20.0, help="target seconds of CPU oracle work")
     ap.add_argument("--dump-index", default="", help="write the block index of the last step to this .npz")
+    ap.add_argument("--no-infer", action="store_true", help="skip the forward-only inference timing")
     ap.add_argument("--a2v-channels", type=int, default=0,
                     help="channels of the A2V producer timing (default heads * head_dim)")
     ap.add_argument("--calibrate-copy", action="store_true",
@@ -263,6 +264,46 @@ def main():
     log("a2v producer", producer)
     del hh
 
+    # forward-only inference path: the 720p forward-only clip and this
+    # workload, against the training path's device bytes
+    infer = None
+    if not args.no_infer:
+        from dynamic_block_sparse_macro_amd.pipeline import PrismInference, training_path_bytes
+        infer = {}
+        for wname in ("720p", args.workload):
+            if wname in infer:
+                continue
+            if wname == args.workload:
+                wi, qi, ki, vi, ai, lay, nnz_i = wl, q, k, v, a, layer, sum(nnz)
+            else:
+                wi = generate(CONFIGS[wname])
+                qi, ki, vi = (tdev(b) for b in (wi.q_bits, wi.k_bits, wi.v_bits))
+                ai = torch.from_numpy(wi.a).to(dev)
+                ci = wi.cfg
+                pi = B.make_params(top_k=ci.top_k, top_p=ci.top_p, density_cap=ci.density_cap)
+                lay = PrismLayer(LayerShape(ci.T, ci.H, ci.W, ci.heads, ci.head_dim), pi, device=dev)
+                nnz_i = sum(lay.forward(qi, ki, vi, ai, torch.empty_like(qi)))
+            ci = wi.cfg
+            inf = PrismInference(lay.shape, lay.params, device=dev)
+            oi = torch.empty_like(qi)
+            inf.forward(qi, ki, vi, ai, oi)
+            torch.cuda.synchronize()
+            reps = 5
+            e = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+            e[0].record(stream)
+            for _ in range(reps):
+                inf.forward(qi, ki, vi, ai, oi)
+            e[1].record(stream)
+            torch.cuda.synchronize()
+            ms = e[0].elapsed_time(e[1]) / reps
+            tr = training_path_bytes(lay, int(nnz_i))
+            infer[wname] = dict(tokens=ci.N, heads=ci.heads, ms=round(ms, 3), ms_per_head=round(ms / ci.heads, 3),
+                                workspace_bytes=inf.ws_bytes.value, training_path_bytes=tr["total"],
+                                memory_saving=round(1 - inf.ws_bytes.value / tr["total"], 4))
+            log("inference", wname, infer[wname])
+            del inf, oi
+        torch.cuda.empty_cache()
+
     cpu = None
     if not args.no_cpu:
         import oracle as O
@@ -305,6 +346,7 @@ def main():
         "speedup_vs_dense": (round(dense["ms_per_head"] / (ms_step / heads), 2) if dense else None),
         "cpu_baseline": cpu,
         "a2v_producer": producer,
+        "inference": infer,
         "wall_s_timed": round(wall, 3),
     }
     print(json.dumps(line), flush=True)

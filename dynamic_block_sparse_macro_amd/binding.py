@@ -32,7 +32,8 @@ VARIANT_AUDIO_ONLY = 16
 VARIANT_RHO_MAX_AUDIO = 32
 
 ENTRY_POINTS = ("prism_zone_stats", "prism_plan_shapes", "prism_select_blocks", "prism_attn_fwd",
-                "prism_attn_bwd", "prism_dense_attn_fwd", "prism_dense_attn_bwd", "prism_a2v_norms", "prism_strerror")
+                "prism_attn_bwd", "prism_dense_attn_fwd", "prism_dense_attn_bwd", "prism_a2v_norms", "prism_infer_fwd",
+                "prism_strerror")
 
 
 class PrismError(RuntimeError):
@@ -51,7 +52,7 @@ class Params(ctypes.Structure):
     _fields_ = [("eps", ctypes.c_double), ("tau128", ctypes.c_double), ("tau256", ctypes.c_double),
                 ("top_k", ctypes.c_int32), ("variant", ctypes.c_int32), ("top_p", ctypes.c_double),
                 ("density_cap", ctypes.c_double), ("scale", ctypes.c_double),
-                ("fixed_shape", ctypes.c_int32), ("reserved", ctypes.c_int32)]
+                ("fixed_shape", ctypes.c_int32), ("pass_heads", ctypes.c_int32)]
 
 
 def make_problem(T, H, W, heads, head_dim, head_stride=None, token_stride=None) -> Problem:
@@ -61,8 +62,8 @@ def make_problem(T, H, W, heads, head_dim, head_stride=None, token_stride=None) 
 
 
 def make_params(top_k=16, top_p=0.9, density_cap=1.0, eps=1e-6, tau128=0.5, tau256=0.25, scale=0.0,
-                variant=0, fixed_shape=0) -> Params:
-    return Params(eps, tau128, tau256, top_k, variant, top_p, density_cap, scale, fixed_shape, 0)
+                variant=0, fixed_shape=0, pass_heads=0) -> Params:
+    return Params(eps, tau128, tau256, top_k, variant, top_p, density_cap, scale, fixed_shape, pass_heads)
 
 
 _lib = None
@@ -89,6 +90,7 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         "prism_dense_attn_fwd": [pp, pr, _vp, _vp, _vp, _vp, _vp, _vp, _P(ctypes.c_size_t), _vp],
         "prism_dense_attn_bwd": [pp, pr] + [_vp] * 10 + [_P(ctypes.c_size_t), _vp],
         "prism_a2v_norms": [_vp, ctypes.c_int64, ctypes.c_int32, ctypes.c_int64, _vp, _vp],
+        "prism_infer_fwd": [pp, pr, _vp, _vp, _vp, _vp, _vp, _vp, _P(ctypes.c_size_t), _vp],
     }
     for name, args in sig.items():
         f = getattr(lib, name)
@@ -190,3 +192,9 @@ def prism_a2v_norms(h_hat, n_tokens, channels, token_stride, a, stream=None, che
     st = load_library().prism_a2v_norms(_ptr(h_hat), int(n_tokens), int(channels), int(token_stride), _ptr(a),
                                         _stream(stream))
     return _check("prism_a2v_norms", st) if check else st
+
+
+def prism_infer_fwd(prob, par, q, k, v, a, o, ws, ws_bytes, stream=None, check=True):
+    st = load_library().prism_infer_fwd(ctypes.byref(prob), ctypes.byref(par), _ptr(q), _ptr(k), _ptr(v), _ptr(a),
+                                        _ptr(o), _ptr(ws), _ref(ws_bytes), _stream(stream))
+    return _check("prism_infer_fwd", st) if check else st

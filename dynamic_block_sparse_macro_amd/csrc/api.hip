@@ -6,6 +6,8 @@
 #include <stdint.h>
 #include <string.h>
 
+#include <vector>
+
 #include "prism_internal.h"
 
 using prism::Geometry;
@@ -51,6 +53,7 @@ int check_params(const prism_params* p) {
   if ((p->variant & PRISM_VARIANT_TOPK_ONLY) && (p->variant & PRISM_VARIANT_TOPP_ONLY)) return PRISM_EPARAM;
   if ((p->variant & PRISM_VARIANT_VISUAL_ONLY) && (p->variant & PRISM_VARIANT_AUDIO_ONLY)) return PRISM_EPARAM;
   if ((p->variant & PRISM_VARIANT_FIXED_SHAPE) && (p->fixed_shape < 0 || p->fixed_shape > 15)) return PRISM_EPARAM;
+  if (p->pass_heads < 0) return PRISM_EPARAM;
   return PRISM_OK;
 }
 
@@ -79,6 +82,55 @@ size_t select_ws(const Geometry& g) {
 size_t operand_bytes(const Geometry& g) { return align256(sizeof(uint16_t) * g.heads * g.N * g.D); }
 
 size_t bwd_ws(const Geometry& g) { return operand_bytes(g) + 2 * align256(sizeof(float) * g.heads * g.N); }
+
+// ---- forward-only inference path ----
+// Heads run in passes of `group` heads, enough for the attention grid to
+// fill the chip (about 2048 workgroups of two 64-token tiles); the workspace
+// holds one pass and is reused by the next.  Inside a pass the float64 tile
+// sums, pooled means and selection scratch are dead once the index is built,
+// so the permuted V rows are written over them.
+struct InferLayout {
+  int group;
+  int64_t lmax;  // largest possible selected blocks per query block
+  size_t zst, gv, rho, shape, perm, bs, nb, qp, kp, region, rp, col, total;
+};
+
+int64_t max_row_blocks(const Geometry& g, const prism_params& p) {
+  const int64_t tiles = g.tiles;
+  if (p.variant & PRISM_VARIANT_TOPK_ONLY) return p.top_k < tiles ? p.top_k : tiles;
+  if (p.density_cap >= 1.0 || p.top_p >= 1.0) return tiles;
+  // the cap admits at most floor(cap N) key tokens beyond Top-k, and every
+  // block holds at least 64 tokens
+  const int64_t cap_blocks = (int64_t)floor(p.density_cap * (double)g.N) / 64;
+  int64_t l = cap_blocks > p.top_k ? cap_blocks : p.top_k;
+  if (l < 1) l = 1;
+  return l < tiles ? l : tiles;
+}
+
+InferLayout infer_layout(const Geometry& geo, const prism_params& p) {
+  InferLayout L;
+  const int64_t want = p.pass_heads > 0 ? p.pass_heads : (4096 + geo.tiles - 1) / geo.tiles;
+  L.group = (int)(want < geo.heads ? want : geo.heads);
+  Geometry g = geo;
+  g.heads = L.group;
+  const int64_t G = L.group;
+  L.lmax = max_row_blocks(geo, p);
+  L.zst = align256(sizeof(double) * G * g.Z * 8);
+  L.gv = align256(sizeof(double) * G * g.Z * 3);
+  L.rho = align256(sizeof(double) * G * g.Z);
+  L.shape = align256(G * g.Z);
+  L.perm = align256(sizeof(int32_t) * G * g.N);
+  L.bs = align256(sizeof(int32_t) * G * (g.tiles + 1));
+  L.nb = align256(sizeof(int32_t) * G);
+  L.qp = operand_bytes(g);
+  L.kp = operand_bytes(g);
+  const size_t sel = select_ws(g);
+  L.region = sel > operand_bytes(g) ? sel : operand_bytes(g);
+  L.rp = align256(sizeof(int32_t) * G * (g.tiles + 1));
+  L.col = align256(sizeof(int32_t) * G * g.tiles * L.lmax);
+  L.total = L.zst + L.gv + L.rho + L.shape + L.perm + L.bs + L.nb + L.qp + L.kp + L.region + L.rp + L.col;
+  return L;
+}
 
 }  // namespace
 
@@ -202,6 +254,73 @@ int prism_attn_bwd(const prism_problem* prob, const prism_params* par, const pri
   HIPCALL(prism::launch_bwd_pre(geo, o, dout, perm, lse, dop, delta, lse2, s));
   HIPCALL(prism::launch_attn_bwd(geo, attn_scale(*par, geo.D), qp, kp, vp, dop, lse2, delta, perm, blk_start,
                                  n_blocks, row_ptr, col_idx, t_row_ptr, t_col_idx, dq, dk, dv, s));
+  return PRISM_OK;
+}
+
+int prism_infer_fwd(const prism_problem* prob, const prism_params* par, const prism_bf16* q, const prism_bf16* k,
+                    const prism_bf16* v, const float* a, prism_bf16* o, void* ws, size_t* ws_bytes,
+                    prism_stream stream) {
+  Geometry geo;
+  CHECK(check_problem(prob, &geo));
+  CHECK(check_params(par));
+  if (!ws_bytes) return PRISM_EINVAL;
+  const InferLayout L = infer_layout(geo, *par);
+  if ((int64_t)L.group * geo.tiles * L.lmax > (int64_t)INT32_MAX) return PRISM_EINVAL;
+  if (!ws) {
+    *ws_bytes = L.total;
+    return PRISM_OK;
+  }
+  if (*ws_bytes < L.total) return PRISM_EWORKSPACE;
+  if (!q || !k || !v || !o) return PRISM_EINVAL;
+  // o may be q, k or v itself: a pass consumes its heads' inputs (zone
+  // statistics, permutation) before its attention writes their outputs
+
+  hipStream_t s = (hipStream_t)stream;
+  char* w = (char*)ws;
+  auto take = [&w](size_t b) {
+    char* r = w;
+    w += b;
+    return r;
+  };
+  double* zst = (double*)take(L.zst);
+  double* gv = (double*)take(L.gv);
+  double* rho = (double*)take(L.rho);
+  uint8_t* shape = (uint8_t*)take(L.shape);
+  int32_t* perm = (int32_t*)take(L.perm);
+  int32_t* bs = (int32_t*)take(L.bs);
+  int32_t* nb = (int32_t*)take(L.nb);
+  uint16_t* qp = (uint16_t*)take(L.qp);
+  uint16_t* kp = (uint16_t*)take(L.kp);
+  char* region = take(L.region);
+  int32_t* rp = (int32_t*)take(L.rp);
+  int32_t* col = (int32_t*)take(L.col);
+  uint16_t* vp = (uint16_t*)region;
+
+  const float scale = attn_scale(*par, geo.D);
+  std::vector<int64_t> nnz(L.group);
+  for (int h0 = 0; h0 < geo.heads; h0 += L.group) {
+    Geometry g = geo;
+    g.heads = geo.heads - h0 < L.group ? geo.heads - h0 : L.group;
+    const int64_t off = (int64_t)h0 * geo.hstride;
+    const size_t pooled = align256(sizeof(double) * g.heads * g.tiles * g.D);
+    double* qsum = (double*)region;
+    double* ksum = (double*)(region + pooled);
+    double* qbar = (double*)(region + 2 * pooled);
+    double* kbar = (double*)(region + 3 * pooled);
+    char* sel = region + 4 * pooled;
+    HIPCALL(prism::launch_zone_stats(g, *par, v + off, a, zst, gv, rho, s));
+    HIPCALL(prism::launch_plan_shapes(g, *par, gv, rho, shape, perm, bs, nb, s));
+    HIPCALL(prism::launch_permute(g, q + off, perm, qp, qsum, s));
+    HIPCALL(prism::launch_permute(g, k + off, perm, kp, ksum, s));
+    HIPCALL(prism::launch_pool_finalize(g, qsum, bs, nb, qbar, s));
+    HIPCALL(prism::launch_pool_finalize(g, ksum, bs, nb, kbar, s));
+    int status = PRISM_OK;
+    HIPCALL(prism::run_selection(g, *par, bs, nb, qbar, kbar, rp, col, (int64_t)g.heads * g.tiles * L.lmax, nullptr,
+                                 nullptr, nnz.data(), sel, &status, s));
+    if (status != PRISM_OK) return status;
+    HIPCALL(prism::launch_permute(g, v + off, perm, vp, nullptr, s));
+    HIPCALL(prism::launch_attn_fwd(g, scale, qp, kp, vp, perm, bs, nb, rp, col, o + off, nullptr, s));
+  }
   return PRISM_OK;
 }
 

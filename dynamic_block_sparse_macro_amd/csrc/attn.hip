@@ -404,7 +404,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(
 
   const float l_tot = l_run + __shfl_xor(l_run, 32, 64);
   const float inv = 1.0f / (r_run + __shfl_xor(r_run, 32, 64));
-  if (g32 == 0) lse[hN + qt * kTile + rloc] = (m_run + __log2f(l_tot)) * kLn2;
+  if (lse != nullptr && g32 == 0) lse[hN + qt * kTile + rloc] = (m_run + __log2f(l_tot)) * kLn2;
   __syncthreads();
   uint16_t* st = (uint16_t*)&smem[0][0][0];       // 128 x (D + 8) staging rows
   acc_to_stage<D>(st, oacc, 32 * w + l32, g32, inv);

@@ -34,6 +34,9 @@ hipError_t launch_permute(const Geometry& g, const uint16_t* x, const int32_t* p
 hipError_t launch_pool_finalize(const Geometry& g, const double* tile_sums, const int32_t* blk_start,
                                 const int32_t* n_blocks, double* pooled, hipStream_t s);
 size_t select_workspace_bytes(const Geometry& g);
+// Scores, selects and writes the query-major index (and, when t_row_ptr is
+// not NULL, the key-major one).  Sets *status to PRISM_ECAPACITY, writing no
+// index, when the pairs exceed col_cap.  Synchronises the stream.
 hipError_t run_selection(const Geometry& g, const prism_params& p, const int32_t* blk_start,
                          const int32_t* n_blocks, const double* qbar, const double* kbar, int32_t* row_ptr,
                          int32_t* col_idx, int64_t col_cap, int32_t* t_row_ptr, int32_t* t_col_idx,
@@ -41,7 +44,7 @@ hipError_t run_selection(const Geometry& g, const prism_params& p, const int32_t
 
 // ---- attention (attn.hip) ----
 // Sparse when row_ptr != NULL, dense over all tiles (64-token blocks, identity
-// perm) otherwise.
+// perm) otherwise.  lse may be NULL (not stored).
 hipError_t launch_attn_fwd(const Geometry& g, float scale, const uint16_t* qp, const uint16_t* kp,
                            const uint16_t* vp, const int32_t* perm, const int32_t* blk_start,
                            const int32_t* n_blocks, const int32_t* row_ptr, const int32_t* col_idx, uint16_t* o,

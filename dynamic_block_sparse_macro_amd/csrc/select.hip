@@ -444,6 +444,11 @@ hipError_t run_selection(const Geometry& g, const prism_params& p, const int32_t
   hipLaunchKernelGGL(emit_rows_kernel, dim3((unsigned)nbmax, (unsigned)g.heads), dim3(64), 0, s, w.bitmap,
                      nbmax * nbw, (int)nbw, n_blocks, w.row_local, g.tiles, w.nnz, col_idx);
   PRISM_TRY(hipGetLastError());
+  dim3 gb((unsigned)((g.tiles + 1 + 255) / 256), (unsigned)g.heads);
+  if (t_row_ptr == nullptr) {  // forward-only caller: no key-major index
+    hipLaunchKernelGGL(add_base_kernel, gb, dim3(256), 0, s, w.row_local, row_ptr, g.tiles, w.nnz);
+    return hipGetLastError();
+  }
   hipLaunchKernelGGL(transpose_kernel, dim3((unsigned)nbw, (unsigned)g.heads), dim3(64), 0, s, w.bitmap, nbmax * nbw,
                      (int)nbw, n_blocks, false, w.t_len, w.t_local, g.tiles, w.nnz, t_col_idx);
   PRISM_TRY(hipGetLastError());
@@ -453,7 +458,6 @@ hipError_t run_selection(const Geometry& g, const prism_params& p, const int32_t
   hipLaunchKernelGGL(transpose_kernel, dim3((unsigned)nbw, (unsigned)g.heads), dim3(64), 0, s, w.bitmap, nbmax * nbw,
                      (int)nbw, n_blocks, true, w.t_len, w.t_local, g.tiles, w.t_nnz, t_col_idx);
   PRISM_TRY(hipGetLastError());
-  dim3 gb((unsigned)((g.tiles + 1 + 255) / 256), (unsigned)g.heads);
   hipLaunchKernelGGL(add_base_kernel, gb, dim3(256), 0, s, w.row_local, row_ptr, g.tiles, w.nnz);
   PRISM_TRY(hipGetLastError());
   hipLaunchKernelGGL(add_base_kernel, gb, dim3(256), 0, s, w.t_local, t_row_ptr, g.tiles, w.t_nnz);

@@ -148,6 +148,41 @@ class PrismLayer:
         return out
 
 
+class PrismInference:
+    """The forward-only layer (prism_infer_fwd): one call, one workspace, no
+    LSE and no key-major index kept.  forward(q, k, v, a, o) may run in
+    place (o is q)."""
+
+    def __init__(self, shape: LayerShape, params: B.Params, device="cuda", head_stride: int | None = None,
+                 token_stride: int | None = None):
+        s = shape
+        self.shape = s
+        self.params = params
+        self.device = device
+        self.prob = B.make_problem(s.T, s.H, s.W, s.heads, s.head_dim, head_stride, token_stride)
+        self.ws_bytes = ctypes.c_size_t(0)
+        B.prism_infer_fwd(self.prob, params, None, None, None, None, None, None, self.ws_bytes)
+        self.ws = torch.empty(self.ws_bytes.value, dtype=torch.uint8, device=device)
+
+    def forward(self, q, k, v, a, o):
+        B.prism_infer_fwd(self.prob, self.params, q, k, v, a, o, self.ws, self.ws_bytes,
+                          torch.cuda.current_stream(self.device))
+
+
+def training_path_bytes(layer: "PrismLayer", nnz_total: int) -> dict:
+    """Device bytes of the training path per layer beyond the caller's
+    tensors: what the forward keeps for the backward (permuted operands,
+    LSE, permutation, block starts, both block indices sized to the selected
+    pairs) and the larger of the two transient workspaces (selection,
+    backward), which a caller can share."""
+    s = layer.shape
+    h, N, D, t, Z = s.heads, s.N, s.head_dim, s.tiles, s.Z
+    kept = (3 * h * N * D * 2 + h * N * 4 + h * N * 4 + h * (t + 1) * 4 + h * 4 + 2 * h * (t + 1) * 4
+            + 2 * nnz_total * 4 + h * Z * (8 + 3 + 1) * 8 + h * Z)
+    transient = max(layer.sel_ws_bytes.value, layer.bwd_ws_bytes.value)
+    return dict(kept=kept, transient=transient, total=kept + transient)
+
+
 class DenseAttention:
     """Full attention on the same kernels (every key tile selected)."""
 

@@ -50,7 +50,7 @@ enum prism_status {
   PRISM_EINVAL = -1,     /* NULL pointer, non-positive size, bad stride, grid too large */
   PRISM_EGRID = -2,      /* T, H or W not a positive multiple of 8 (zones do not overlap [pt/IC]) */
   PRISM_EDIM = -3,       /* head_dim not 64 or 128 */
-  PRISM_EPARAM = -4,     /* eps <= 0, tau256 > tau128, top_k < 1, top_p or density_cap outside (0, 1], scale < 0, bad variant */
+  PRISM_EPARAM = -4,     /* eps <= 0, tau256 > tau128, top_k < 1, top_p or density_cap outside (0, 1], scale < 0, bad variant or pass_heads < 0 */
   PRISM_ECAPACITY = -5,  /* col_cap smaller than the number of selected (query block, key block) pairs */
   PRISM_EWORKSPACE = -6, /* workspace NULL-with-size or too small */
   PRISM_EHIP = -7        /* a HIP runtime call failed */
@@ -86,7 +86,7 @@ typedef struct prism_params {
   double density_cap;  /* in (0, 1]; at most floor(cap * N) key tokens per query block beyond Top-k; 1 = none */
   double scale;        /* softmax scale of block scores and attention; 0 -> 1/sqrt(head_dim) */
   int32_t fixed_shape; /* shape index 0..15 for PRISM_VARIANT_FIXED_SHAPE */
-  int32_t reserved;
+  int32_t pass_heads;  /* prism_infer_fwd: heads per pass, >= 0; 0 = automatic */
 } prism_params;
 
 /* Candidate shapes, index 0..15: edges in {2,4,8}, volume in {64,128,256}
@@ -205,6 +205,32 @@ int prism_attn_bwd(const prism_problem *prob, const prism_params *par, const pri
                    const int32_t *perm, const int32_t *blk_start, const int32_t *n_blocks, const int32_t *row_ptr,
                    const int32_t *col_idx, const int32_t *t_row_ptr, const int32_t *t_col_idx, prism_bf16 *dq,
                    prism_bf16 *dk, prism_bf16 *dv, void *ws, size_t *ws_bytes, prism_stream stream);
+
+/*
+ * prism_infer_fwd -- the whole forward layer for inference in one call:
+ * zone statistics, shapes, permutation, block selection (query-major index
+ * only) and sparse attention ([pt/M1]-[pt/M3]), output scattered back to THW
+ * ([blog/4]: inference reuses the dynamic sparse logic to save memory).
+ * Nothing is kept for a backward pass: no LSE, no key-major index.
+ *
+ * q, k, v  THW bf16 inputs; a as in prism_zone_stats (NULL = no audio).
+ * o        THW bf16 (out).  o may be the same buffer as q, k or v (in place,
+ *          element for element); any other overlap is undefined.
+ * ws, ws_bytes  workspace (with ws == NULL only the size is stored).  Heads
+ *          are processed in passes of par->pass_heads heads (0: enough for
+ *          the attention grid to fill the chip, ceil(4096 / (N/64)); at most
+ *          all of them) whose intermediates share one workspace; inside a pass
+ *          the permuted V rows reuse the memory of the selection scratch.
+ *          The block index is sized for the most blocks a row can select
+ *          (every block with top_p = 1 and no cap; else max(top_k,
+ *          floor(cap N) / 64) blocks), so the call never returns
+ *          PRISM_ECAPACITY.
+ * Results equal those of prism_zone_stats .. prism_attn_fwd on the same
+ * inputs bit for bit.  Synchronises the stream once per pass.
+ */
+int prism_infer_fwd(const prism_problem *prob, const prism_params *par, const prism_bf16 *q, const prism_bf16 *k,
+                    const prism_bf16 *v, const float *a, prism_bf16 *o, void *ws, size_t *ws_bytes,
+                    prism_stream stream);
 
 /*
  * prism_dense_attn_fwd / prism_dense_attn_bwd -- full softmax attention over

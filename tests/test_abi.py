@@ -118,3 +118,26 @@ def test_a2v_norms_validation(lib):
         assert B.prism_a2v_norms(check=False, **kw) == B.PRISM_EINVAL, over
     # no rows: nothing to do, no launch
     assert B.prism_a2v_norms(256, 0, 64, 64, 256, check=False) == B.PRISM_OK
+
+
+def test_infer_workspace_and_validation(lib):
+    """prism_infer_fwd: size query, the heads-per-pass knob, and rejection
+    of bad arguments before any launch."""
+    prob = _prob()
+    n1, n2, n0 = ctypes.c_size_t(0), ctypes.c_size_t(0), ctypes.c_size_t(0)
+    assert B.prism_infer_fwd(prob, B.make_params(pass_heads=1), *([None] * 6), n1, check=False) == B.PRISM_OK
+    assert B.prism_infer_fwd(prob, B.make_params(pass_heads=2), *([None] * 6), n2, check=False) == B.PRISM_OK
+    assert B.prism_infer_fwd(prob, B.make_params(), *([None] * 6), n0, check=False) == B.PRISM_OK
+    N, D = 16 * 16 * 16, 128
+    # one pass holds Q and K in operand layout plus the larger of V and the selection scratch
+    assert n1.value >= 3 * N * D * 2
+    assert n2.value >= 2 * n1.value - 4096 * 8 * 12
+    assert n0.value == n2.value          # 64 tiles: one pass holds both heads
+    assert B.prism_infer_fwd(prob, B.make_params(pass_heads=-1), *([None] * 6), n1,
+                             check=False) == B.PRISM_EPARAM
+    assert B.prism_infer_fwd(prob, B.make_params(), *([None] * 6), None, check=False) == B.PRISM_EINVAL
+    small = ctypes.c_size_t(n0.value - 1)
+    assert B.prism_infer_fwd(prob, B.make_params(), 16, 16, 16, None, 16, 16, small,
+                             check=False) == B.PRISM_EWORKSPACE
+    ok = ctypes.c_size_t(n0.value)
+    assert B.prism_infer_fwd(prob, B.make_params(), 16, None, 16, None, 16, 16, ok, check=False) == B.PRISM_EINVAL
