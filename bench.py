@@ -29,6 +29,24 @@ sys.path.insert(0, ROOT)
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
 PEAK_HBM_GBS = 8000.0
 
+# HBM bytes per launch of attn_fwd_kernel at the 2K workload (both heads):
+# FETCH_SIZE x 2.000 + WRITE_SIZE, the factors read from plain 1 GiB copy
+# kernels in the same counter runs.  Valid only for the kernel source the
+# counters were taken on (hash of attn.hip + prism_device.h); reported as
+# null for any other source or workload.
+FWD_TRAFFIC = dict(workload="2k", bytes=95_919_364 * 1024,
+                   source_sha256="f7ca3639272779675bba2209f866548ce2a9e58241f09d938f245f18a1a30fff")
+
+
+def attn_source_sha256() -> str:
+    import hashlib
+    h = hashlib.sha256()
+    base = os.path.join(os.path.dirname(os.path.abspath(__file__)), "dynamic_block_sparse_macro_amd", "csrc")
+    for f in ("attn.hip", "prism_device.h"):
+        with open(os.path.join(base, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
 
 def log(*a):
     print(f"[bench {time.strftime('%H:%M:%S')}]", *a, file=sys.stderr, flush=True)
@@ -152,9 +170,13 @@ def main():
     dq, dk, dv = (torch.empty_like(q) for _ in range(3))
     layer = PrismLayer(shape, par, device=dev)
     if args.calibrate_copy:
-        src = torch.empty(512 << 20, dtype=torch.uint8, device=dev).fill_(1)
+        # plain copy kernels of known size for scaling the HBM byte counters:
+        # 1 GiB fill (write only), 1 GiB device copy, 1 GiB float32 negation
+        # (read 1 GiB, write 1 GiB); larger than the 256 MB last-level cache
+        src = torch.empty(1 << 30, dtype=torch.uint8, device=dev).fill_(1)
         dst = torch.empty_like(src)
         dst.copy_(src)
+        torch.neg(src.view(torch.float32), out=dst.view(torch.float32))
         torch.cuda.synchronize()
         del src, dst
     stream = torch.cuda.current_stream(dev)
@@ -313,9 +335,12 @@ def main():
         log("cpu", cpu)
 
     fwd_ms = stage_ms["attn_fwd"]
+    traffic = None
+    if args.workload == FWD_TRAFFIC["workload"] and attn_source_sha256() == FWD_TRAFFIC["source_sha256"]:
+        traffic = FWD_TRAFFIC["bytes"]
     roof = dict(bound="mfma", kernel="attn_fwd_kernel<128,sparse>", achieved=round(fwd_tflops, 1),
-                peak=PEAK_BF16_TFLOPS, unit="TFLOP/s", frac=round(fwd_tflops / PEAK_BF16_TFLOPS, 4), traffic=None,
-                flops_per_launch=f_fwd, launch_ms=round(fwd_ms, 4))
+                peak=PEAK_BF16_TFLOPS, unit="TFLOP/s", frac=round(fwd_tflops / PEAK_BF16_TFLOPS, 4), traffic=traffic,
+                traffic_unit="bytes per launch", flops_per_launch=f_fwd, launch_ms=round(fwd_ms, 4))
     line = {
         "metric": "fwd+bwd ms per head at 450K tokens; achieved MFMA TFLOP/s (% of peak)",
         "value": round(ms_step / heads, 3),
