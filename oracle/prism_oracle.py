@@ -52,6 +52,16 @@ design notes):
   R15 statistics, shapes and the block index are per head; a is shared.
   R16 no causal mask; the log-sum-exp uses the natural log.
   R17 no block is forced into S_i.
+  R21 ablation variants (sd114.wiki post, "测试结果" items 2-3, which compare
+      fixed block shapes, video-only and audio-only guidance, and Top-k-only
+      or adaptive-threshold-only selection): a fixed shape replaces the plan
+      in every zone; Top-k alone keeps min(k, n_b) blocks; Top-p alone keeps
+      the (capped) nucleus, at least one block; video-only guidance drops the
+      a-bar v-hat term, audio-only guidance drops r; max(rho, a-bar) is an
+      alternative density.  (max(rho, a-bar): parity unpinned; the others
+      reduce to the method's own rule or to closed cases in the pins.)
+  R22 the A2V norm a_n = |h-hat_n|_2 is taken over the bf16 values of h-hat
+      in float64 (squares exact) and rounded once to float32.
 """
 
 from __future__ import annotations
