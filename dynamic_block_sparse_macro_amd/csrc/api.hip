@@ -83,6 +83,9 @@ size_t operand_bytes(const Geometry& g) { return align256(sizeof(uint16_t) * g.h
 
 size_t bwd_ws(const Geometry& g) { return operand_bytes(g) + 2 * align256(sizeof(float) * g.heads * g.N); }
 
+// work-queue counters of the persistent attention kernels
+constexpr size_t kQueueBytes = sizeof(int) * prism::kQueueInts;
+
 // ---- forward-only inference path ----
 // Heads run in passes of `group` heads, enough for the attention grid to
 // fill the chip (about 2048 workgroups of two 64-token tiles); the workspace
@@ -92,7 +95,7 @@ size_t bwd_ws(const Geometry& g) { return operand_bytes(g) + 2 * align256(sizeof
 struct InferLayout {
   int group;
   int64_t lmax;  // largest possible selected blocks per query block
-  size_t zst, gv, rho, shape, perm, bs, nb, qp, kp, region, rp, col, total;
+  size_t zst, gv, rho, shape, perm, bs, nb, qp, kp, region, rp, col, queues, total;
 };
 
 int64_t max_row_blocks(const Geometry& g, const prism_params& p) {
@@ -128,7 +131,8 @@ InferLayout infer_layout(const Geometry& geo, const prism_params& p) {
   L.region = sel > operand_bytes(g) ? sel : operand_bytes(g);
   L.rp = align256(sizeof(int32_t) * G * (g.tiles + 1));
   L.col = align256(sizeof(int32_t) * G * g.tiles * L.lmax);
-  L.total = L.zst + L.gv + L.rho + L.shape + L.perm + L.bs + L.nb + L.qp + L.kp + L.region + L.rp + L.col;
+  L.queues = align256(kQueueBytes);
+  L.total = L.zst + L.gv + L.rho + L.shape + L.perm + L.bs + L.nb + L.qp + L.kp + L.region + L.rp + L.col + L.queues;
   return L;
 }
 
@@ -218,14 +222,22 @@ int prism_select_blocks(const prism_problem* prob, const prism_params* par, cons
 
 int prism_attn_fwd(const prism_problem* prob, const prism_params* par, const prism_bf16* qp, const prism_bf16* kp,
                    const prism_bf16* vp, const int32_t* perm, const int32_t* blk_start, const int32_t* n_blocks,
-                   const int32_t* row_ptr, const int32_t* col_idx, prism_bf16* o, float* lse, prism_stream stream) {
+                   const int32_t* row_ptr, const int32_t* col_idx, prism_bf16* o, float* lse, void* ws,
+                   size_t* ws_bytes, prism_stream stream) {
   Geometry geo;
   CHECK(check_problem(prob, &geo));
   CHECK(check_params(par));
+  if (!ws_bytes) return PRISM_EINVAL;
+  const size_t need = align256(kQueueBytes);
+  if (!ws) {
+    *ws_bytes = need;
+    return PRISM_OK;
+  }
+  if (*ws_bytes < need) return PRISM_EWORKSPACE;
   if (!qp || !kp || !vp || !perm || !blk_start || !n_blocks || !row_ptr || !col_idx || !o || !lse)
     return PRISM_EINVAL;
   HIPCALL(prism::launch_attn_fwd(geo, attn_scale(*par, geo.D), qp, kp, vp, perm, blk_start, n_blocks, row_ptr,
-                                 col_idx, o, lse, (hipStream_t)stream));
+                                 col_idx, o, lse, (int*)ws, (hipStream_t)stream));
   return PRISM_OK;
 }
 
@@ -238,7 +250,7 @@ int prism_attn_bwd(const prism_problem* prob, const prism_params* par, const pri
   CHECK(check_problem(prob, &geo));
   CHECK(check_params(par));
   if (!ws_bytes) return PRISM_EINVAL;
-  const size_t need = bwd_ws(geo);
+  const size_t need = bwd_ws(geo) + align256(kQueueBytes);
   if (!ws) {
     *ws_bytes = need;
     return PRISM_OK;
@@ -251,9 +263,10 @@ int prism_attn_bwd(const prism_problem* prob, const prism_params* par, const pri
   uint16_t* dop = (uint16_t*)ws;
   float* delta = (float*)((char*)ws + operand_bytes(geo));
   float* lse2 = (float*)((char*)delta + align256(sizeof(float) * geo.heads * geo.N));
+  int* queues = (int*)((char*)ws + bwd_ws(geo));
   HIPCALL(prism::launch_bwd_pre(geo, o, dout, perm, lse, dop, delta, lse2, s));
   HIPCALL(prism::launch_attn_bwd(geo, attn_scale(*par, geo.D), qp, kp, vp, dop, lse2, delta, perm, blk_start,
-                                 n_blocks, row_ptr, col_idx, t_row_ptr, t_col_idx, dq, dk, dv, s));
+                                 n_blocks, row_ptr, col_idx, t_row_ptr, t_col_idx, dq, dk, dv, queues, s));
   return PRISM_OK;
 }
 
@@ -294,6 +307,7 @@ int prism_infer_fwd(const prism_problem* prob, const prism_params* par, const pr
   char* region = take(L.region);
   int32_t* rp = (int32_t*)take(L.rp);
   int32_t* col = (int32_t*)take(L.col);
+  int* queues = (int*)take(L.queues);
   uint16_t* vp = (uint16_t*)region;
 
   const float scale = attn_scale(*par, geo.D);
@@ -319,7 +333,7 @@ int prism_infer_fwd(const prism_problem* prob, const prism_params* par, const pr
                                  nullptr, nnz.data(), sel, &status, s));
     if (status != PRISM_OK) return status;
     HIPCALL(prism::launch_permute(g, v + off, perm, vp, nullptr, s));
-    HIPCALL(prism::launch_attn_fwd(g, scale, qp, kp, vp, perm, bs, nb, rp, col, o + off, nullptr, s));
+    HIPCALL(prism::launch_attn_fwd(g, scale, qp, kp, vp, perm, bs, nb, rp, col, o + off, nullptr, queues, s));
   }
   return PRISM_OK;
 }
@@ -331,7 +345,7 @@ int prism_dense_attn_fwd(const prism_problem* prob, const prism_params* par, con
   CHECK(check_problem(prob, &geo));
   CHECK(check_params(par));
   if (!ws_bytes) return PRISM_EINVAL;
-  const size_t need = 3 * operand_bytes(geo);
+  const size_t need = 3 * operand_bytes(geo) + align256(kQueueBytes);
   if (!ws) {
     *ws_bytes = need;
     return PRISM_OK;
@@ -345,8 +359,9 @@ int prism_dense_attn_fwd(const prism_problem* prob, const prism_params* par, con
   HIPCALL(prism::launch_permute(geo, q, nullptr, qp, nullptr, s));
   HIPCALL(prism::launch_permute(geo, k, nullptr, kp, nullptr, s));
   HIPCALL(prism::launch_permute(geo, v, nullptr, vp, nullptr, s));
+  int* queues = (int*)((char*)ws + 3 * operand_bytes(geo));
   HIPCALL(prism::launch_attn_fwd(geo, attn_scale(*par, geo.D), qp, kp, vp, nullptr, nullptr, nullptr, nullptr,
-                                 nullptr, o, lse, s));
+                                 nullptr, o, lse, queues, s));
   return PRISM_OK;
 }
 
@@ -358,7 +373,7 @@ int prism_dense_attn_bwd(const prism_problem* prob, const prism_params* par, con
   CHECK(check_problem(prob, &geo));
   CHECK(check_params(par));
   if (!ws_bytes) return PRISM_EINVAL;
-  const size_t need = 3 * operand_bytes(geo) + bwd_ws(geo);
+  const size_t need = 3 * operand_bytes(geo) + bwd_ws(geo) + align256(kQueueBytes);
   if (!ws) {
     *ws_bytes = need;
     return PRISM_OK;
@@ -376,9 +391,10 @@ int prism_dense_attn_bwd(const prism_problem* prob, const prism_params* par, con
   HIPCALL(prism::launch_permute(geo, q, nullptr, qp, nullptr, s));
   HIPCALL(prism::launch_permute(geo, k, nullptr, kp, nullptr, s));
   HIPCALL(prism::launch_permute(geo, v, nullptr, vp, nullptr, s));
+  int* queues = (int*)((char*)ws + 3 * ob + bwd_ws(geo));
   HIPCALL(prism::launch_bwd_pre(geo, o, dout, nullptr, lse, dop, delta, lse2, s));
   HIPCALL(prism::launch_attn_bwd(geo, attn_scale(*par, geo.D), qp, kp, vp, dop, lse2, delta, nullptr, nullptr,
-                                 nullptr, nullptr, nullptr, nullptr, nullptr, dq, dk, dv, s));
+                                 nullptr, nullptr, nullptr, nullptr, nullptr, dq, dk, dv, queues, s));
   return PRISM_OK;
 }
 

@@ -25,7 +25,13 @@
 //  * float32 online softmax in the log2 domain with lazy rescaling (the
 //    running maximum moves only when a score exceeds it by 2^8);
 //  * the backward runs a query-major pass (dQ) and a key-major pass over the
-//    transposed block index (dK, dV): no float atomics, bitwise reproducible.
+//    transposed block index (dK, dV): no float atomics, bitwise reproducible;
+//  * persistent workgroups: the grid holds as many workgroups as the chip
+//    keeps resident, and each takes tile pairs from a work queue, first the
+//    queue of its own XCD (one contiguous eighth of the pairs, so neighbouring
+//    query blocks, which share most key blocks, meet in one L2), then the
+//    others.  Rows differ widely in length, so this balances the XCDs and
+//    leaves no slot waiting on the dispatcher.
 
 #include <limits.h>
 
@@ -271,6 +277,51 @@ __device__ __forceinline__ PairIter make_iter(const Geometry& g, int h, int pair
 template <int B>
 using Parity = std::integral_constant<int, B>;
 
+// Work queues of a persistent launch: work items 0..total-1 split into 8
+// contiguous ranges, one per XCD, each with a counter in cnt[0..7] (zero at
+// launch).  A workgroup drains the queue of the XCD it runs on, then the
+// others in turn; every call on an exhausted queue moves on, so each
+// workgroup makes at most total + 8 attempts and always ends.
+struct WorkQueue {
+  int* cnt;
+  int total, per, xq, qi;
+
+  __device__ __forceinline__ void init(int* c, int n) {
+    unsigned x;
+    asm volatile("s_getreg_b32 %0, hwreg(HW_REG_XCC_ID)" : "=s"(x));
+    cnt = c;
+    total = n;
+    per = (n + 7) / 8;
+    xq = (int)(x & 7);
+    qi = 0;
+  }
+  // next work item or -1 (called by one thread)
+  __device__ __forceinline__ int next() {
+    while (qi < 8) {
+      const int q = (xq + qi) & 7;
+      const int lo = q * per;
+      const int hi = lo + per < total ? lo + per : total;
+      if (lo < hi) {
+        const int i = atomicAdd(&cnt[q], 1);
+        if (lo + i < hi) return lo + i;
+      }
+      ++qi;
+    }
+    return -1;
+  }
+};
+
+// the workgroup's next work item (uniform), -1 when all queues are empty
+__device__ __forceinline__ int fetch_work(WorkQueue& wq, int* slot) {
+  if (threadIdx.x == 0) *slot = wq.next();
+  __syncthreads();
+  return *slot;
+}
+
+__global__ void zero_kernel(int* __restrict__ p, int n) {
+  for (int i = threadIdx.x; i < n; i += blockDim.x) p[i] = 0;
+}
+
 // ---------------------------------------------------------------------------
 // forward
 // ---------------------------------------------------------------------------
@@ -279,11 +330,18 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(
     Geometry g, float sl2, const uint16_t* __restrict__ qp, const uint16_t* __restrict__ kp,
     const uint16_t* __restrict__ vp, const int32_t* __restrict__ perm, const int32_t* __restrict__ blk_start,
     const int32_t* __restrict__ n_blocks, const int32_t* __restrict__ row_ptr, const int32_t* __restrict__ col_idx,
-    uint16_t* __restrict__ o, float* __restrict__ lse) {
+    uint16_t* __restrict__ o, float* __restrict__ lse, int* __restrict__ cnt) {
   constexpr int TB = TileGeo<D>::BYTES;
   __shared__ __attribute__((aligned(16))) char smem[2][2][TB];   // [buffer][K, V]
-  const int h = blockIdx.y;
-  const int pair = xcd_remap(blockIdx.x, gridDim.x);
+  __shared__ int s_work;
+  const int npair = (int)(g.tiles / 2);
+  WorkQueue wq;
+  wq.init(cnt, npair * g.heads);
+  for (;;) {
+  const int wk = fetch_work(wq, &s_work);
+  if (wk < 0) break;
+  const int h = wk / npair;
+  const int pair = wk % npair;
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, g32 = lane >> 5, l32 = lane & 31;
   const bool second = w >= 2;
   const int64_t hN = (int64_t)h * g.N;
@@ -410,6 +468,8 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(
   acc_to_stage<D>(st, oacc, 32 * w + l32, g32, inv);
   __syncthreads();
   store_pair_thw<D>(st, o, g, h, 2 * (int64_t)pair, perm);
+  __syncthreads();   // staging area and s_work are reused by the next item
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -459,11 +519,18 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bwd_dq_kernel(
     const uint16_t* __restrict__ vp, const uint16_t* __restrict__ dop, const float* __restrict__ lse2,
     const float* __restrict__ delta, const int32_t* __restrict__ perm, const int32_t* __restrict__ blk_start,
     const int32_t* __restrict__ n_blocks, const int32_t* __restrict__ row_ptr, const int32_t* __restrict__ col_idx,
-    uint16_t* __restrict__ dq) {
+    uint16_t* __restrict__ dq, int* __restrict__ cnt) {
   constexpr int TB = TileGeo<D>::BYTES;
   __shared__ __attribute__((aligned(16))) char smem[2][2][TB];   // [buffer][K, V]
-  const int h = blockIdx.y;
-  const int pair = xcd_remap(blockIdx.x, gridDim.x);
+  __shared__ int s_work;
+  const int npair = (int)(g.tiles / 2);
+  WorkQueue wq;
+  wq.init(cnt, npair * g.heads);
+  for (;;) {
+  const int wk = fetch_work(wq, &s_work);
+  if (wk < 0) break;
+  const int h = wk / npair;
+  const int pair = wk % npair;
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, g32 = lane >> 5, l32 = lane & 31;
   const bool second = w >= 2;
   const int64_t hN = (int64_t)h * g.N;
@@ -559,6 +626,8 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bwd_dq_kernel(
   acc_to_stage<D>(st, dqacc, 32 * w + l32, g32, scale);
   __syncthreads();
   store_pair_thw<D>(st, dq, g, h, 2 * (int64_t)pair, perm);
+  __syncthreads();   // staging area and s_work are reused by the next item
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -570,12 +639,20 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bwd_dkdv_kernel(
     const uint16_t* __restrict__ vp, const uint16_t* __restrict__ dop, const float* __restrict__ lse2,
     const float* __restrict__ delta, const int32_t* __restrict__ perm, const int32_t* __restrict__ blk_start,
     const int32_t* __restrict__ n_blocks, const int32_t* __restrict__ t_row_ptr,
-    const int32_t* __restrict__ t_col_idx, uint16_t* __restrict__ dk, uint16_t* __restrict__ dv) {
+    const int32_t* __restrict__ t_col_idx, uint16_t* __restrict__ dk, uint16_t* __restrict__ dv,
+    int* __restrict__ cnt) {
   constexpr int TB = TileGeo<D>::BYTES;
   __shared__ __attribute__((aligned(16))) char smem[2][2][TB];   // [buffer][Q, dO]
   __shared__ __attribute__((aligned(16))) float svec[2][2][kTile]; // [buffer][lse2, delta]
-  const int h = blockIdx.y;
-  const int pair = xcd_remap(blockIdx.x, gridDim.x);
+  __shared__ int s_work;
+  const int npair = (int)(g.tiles / 2);
+  WorkQueue wq;
+  wq.init(cnt, npair * g.heads);
+  for (;;) {
+  const int wk = fetch_work(wq, &s_work);
+  if (wk < 0) break;
+  const int h = wk / npair;
+  const int pair = wk % npair;
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, g32 = lane >> 5, l32 = lane & 31;
   const bool second = w >= 2;
   const int64_t hN = (int64_t)h * g.N;
@@ -697,15 +774,32 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bwd_dkdv_kernel(
   acc_to_stage<D>(st, dvacc, 32 * w + l32, g32, 1.0f);
   __syncthreads();
   store_pair_thw<D>(st, dv, g, h, 2 * (int64_t)pair, perm);
+  __syncthreads();   // staging area and s_work are reused by the next item
+  }
+}
+
+// workgroups of `kernel` the chip keeps resident at once (the persistent grid)
+hipError_t resident_grid(const void* kernel, unsigned* grid) {
+  int dev = 0, cus = 0, per_cu = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+  if (e == hipSuccess) e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, kThreads, 0);
+  if (e != hipSuccess) return e;
+  *grid = (unsigned)((cus > 0 ? cus : 1) * (per_cu > 0 ? per_cu : 1));
+  return hipSuccess;
 }
 
 template <int D, bool DENSE>
 hipError_t fwd_impl(const Geometry& g, float scale, const uint16_t* qp, const uint16_t* kp, const uint16_t* vp,
                     const int32_t* perm, const int32_t* blk_start, const int32_t* n_blocks, const int32_t* row_ptr,
-                    const int32_t* col_idx, uint16_t* o, float* lse, hipStream_t s) {
-  dim3 grid((unsigned)(g.tiles / 2), (unsigned)g.heads);
-  hipLaunchKernelGGL((attn_fwd_kernel<D, DENSE>), grid, dim3(kThreads), 0, s, g, scale * kLog2e, qp, kp, vp, perm,
-                     blk_start, n_blocks, row_ptr, col_idx, o, lse);
+                    const int32_t* col_idx, uint16_t* o, float* lse, int* queues, hipStream_t s) {
+  const void* k = (const void*)attn_fwd_kernel<D, DENSE>;
+  unsigned grid = 0;
+  hipError_t e = resident_grid(k, &grid);
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(zero_kernel, dim3(1), dim3(64), 0, s, queues, 8);
+  hipLaunchKernelGGL((attn_fwd_kernel<D, DENSE>), dim3(grid), dim3(kThreads), 0, s, g, scale * kLog2e, qp, kp, vp,
+                     perm, blk_start, n_blocks, row_ptr, col_idx, o, lse, queues);
   return hipGetLastError();
 }
 
@@ -714,14 +808,19 @@ hipError_t bwd_impl(const Geometry& g, float scale, const uint16_t* qp, const ui
                     const uint16_t* dop, const float* lse2, const float* delta, const int32_t* perm,
                     const int32_t* blk_start, const int32_t* n_blocks, const int32_t* row_ptr,
                     const int32_t* col_idx, const int32_t* t_row_ptr, const int32_t* t_col_idx, uint16_t* dq,
-                    uint16_t* dk, uint16_t* dv, hipStream_t s) {
-  dim3 grid((unsigned)(g.tiles / 2), (unsigned)g.heads);
-  hipLaunchKernelGGL((attn_bwd_dq_kernel<D, DENSE>), grid, dim3(kThreads), 0, s, g, scale, scale * kLog2e, qp, kp,
-                     vp, dop, lse2, delta, perm, blk_start, n_blocks, row_ptr, col_idx, dq);
-  hipError_t e = hipGetLastError();
+                    uint16_t* dk, uint16_t* dv, int* queues, hipStream_t s) {
+  unsigned grid_q = 0, grid_k = 0;
+  hipError_t e = resident_grid((const void*)attn_bwd_dq_kernel<D, DENSE>, &grid_q);
+  if (e == hipSuccess) e = resident_grid((const void*)attn_bwd_dkdv_kernel<D, DENSE>, &grid_k);
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((attn_bwd_dkdv_kernel<D, DENSE>), grid, dim3(kThreads), 0, s, g, scale, scale * kLog2e, qp, kp,
-                     vp, dop, lse2, delta, perm, blk_start, n_blocks, t_row_ptr, t_col_idx, dk, dv);
+  hipLaunchKernelGGL(zero_kernel, dim3(1), dim3(64), 0, s, queues, 16);
+  hipLaunchKernelGGL((attn_bwd_dq_kernel<D, DENSE>), dim3(grid_q), dim3(kThreads), 0, s, g, scale, scale * kLog2e, qp,
+                     kp, vp, dop, lse2, delta, perm, blk_start, n_blocks, row_ptr, col_idx, dq, queues);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL((attn_bwd_dkdv_kernel<D, DENSE>), dim3(grid_k), dim3(kThreads), 0, s, g, scale, scale * kLog2e,
+                     qp, kp, vp, dop, lse2, delta, perm, blk_start, n_blocks, t_row_ptr, t_col_idx, dk, dv,
+                     queues + 8);
   return hipGetLastError();
 }
 
@@ -730,13 +829,13 @@ hipError_t bwd_impl(const Geometry& g, float scale, const uint16_t* qp, const ui
 hipError_t launch_attn_fwd(const Geometry& g, float scale, const uint16_t* qp, const uint16_t* kp,
                            const uint16_t* vp, const int32_t* perm, const int32_t* blk_start,
                            const int32_t* n_blocks, const int32_t* row_ptr, const int32_t* col_idx, uint16_t* o,
-                           float* lse, hipStream_t s) {
+                           float* lse, int* queues, hipStream_t s) {
   const bool dense = row_ptr == nullptr;
-  if (g.D == 128)
-    return dense ? fwd_impl<128, true>(g, scale, qp, kp, vp, perm, blk_start, n_blocks, row_ptr, col_idx, o, lse, s)
-                 : fwd_impl<128, false>(g, scale, qp, kp, vp, perm, blk_start, n_blocks, row_ptr, col_idx, o, lse, s);
-  return dense ? fwd_impl<64, true>(g, scale, qp, kp, vp, perm, blk_start, n_blocks, row_ptr, col_idx, o, lse, s)
-               : fwd_impl<64, false>(g, scale, qp, kp, vp, perm, blk_start, n_blocks, row_ptr, col_idx, o, lse, s);
+#define PRISM_FWD(DD, DN) \
+  fwd_impl<DD, DN>(g, scale, qp, kp, vp, perm, blk_start, n_blocks, row_ptr, col_idx, o, lse, queues, s)
+  if (g.D == 128) return dense ? PRISM_FWD(128, true) : PRISM_FWD(128, false);
+  return dense ? PRISM_FWD(64, true) : PRISM_FWD(64, false);
+#undef PRISM_FWD
 }
 
 hipError_t launch_bwd_pre(const Geometry& g, const uint16_t* o, const uint16_t* dout, const int32_t* perm,
@@ -753,11 +852,12 @@ hipError_t launch_attn_bwd(const Geometry& g, float scale, const uint16_t* qp, c
                            const uint16_t* vp, const uint16_t* dop, const float* lse2, const float* delta,
                            const int32_t* perm, const int32_t* blk_start, const int32_t* n_blocks,
                            const int32_t* row_ptr, const int32_t* col_idx, const int32_t* t_row_ptr,
-                           const int32_t* t_col_idx, uint16_t* dq, uint16_t* dk, uint16_t* dv, hipStream_t s) {
+                           const int32_t* t_col_idx, uint16_t* dq, uint16_t* dk, uint16_t* dv, int* queues,
+                           hipStream_t s) {
   const bool dense = row_ptr == nullptr;
 #define PRISM_BWD(DD, DN)                                                                                          \
   bwd_impl<DD, DN>(g, scale, qp, kp, vp, dop, lse2, delta, perm, blk_start, n_blocks, row_ptr, col_idx, t_row_ptr, \
-                   t_col_idx, dq, dk, dv, s)
+                   t_col_idx, dq, dk, dv, queues, s)
   if (g.D == 128) return dense ? PRISM_BWD(128, true) : PRISM_BWD(128, false);
   return dense ? PRISM_BWD(64, true) : PRISM_BWD(64, false);
 #undef PRISM_BWD

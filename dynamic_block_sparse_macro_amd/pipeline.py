@@ -79,6 +79,9 @@ class PrismLayer:
         B.prism_select_blocks(self.prob, params, None, None, None, None, None, None, None, None, None, None, None,
                               0, None, None, None, None, self.sel_ws_bytes)
         self.sel_ws = torch.empty(self.sel_ws_bytes.value, dtype=torch.uint8, **dev)
+        self.fwd_ws_bytes = ctypes.c_size_t(0)
+        B.prism_attn_fwd(self.prob, params, *([None] * 11), self.fwd_ws_bytes)
+        self.fwd_ws = torch.empty(self.fwd_ws_bytes.value, dtype=torch.uint8, **dev)
         self.bwd_ws_bytes = ctypes.c_size_t(0)
         B.prism_attn_bwd(self.prob, params, *([None] * 17), self.bwd_ws_bytes)
         self.bwd_ws = None
@@ -111,7 +114,8 @@ class PrismLayer:
 
     def attn_fwd(self, o):
         B.prism_attn_fwd(self.prob, self.params, self.qp, self.kp, self.vp, self.perm, self.blk_start,
-                         self.n_blocks, self.row_ptr, self.col_idx, o, self.lse, self.stream())
+                         self.n_blocks, self.row_ptr, self.col_idx, o, self.lse, self.fwd_ws, self.fwd_ws_bytes,
+                         self.stream())
 
     def attn_bwd(self, o, do, dq, dk, dv):
         if self.bwd_ws is None:
@@ -179,7 +183,7 @@ def training_path_bytes(layer: "PrismLayer", nnz_total: int) -> dict:
     h, N, D, t, Z = s.heads, s.N, s.head_dim, s.tiles, s.Z
     kept = (3 * h * N * D * 2 + h * N * 4 + h * N * 4 + h * (t + 1) * 4 + h * 4 + 2 * h * (t + 1) * 4
             + 2 * nnz_total * 4 + h * Z * (8 + 3 + 1) * 8 + h * Z)
-    transient = max(layer.sel_ws_bytes.value, layer.bwd_ws_bytes.value)
+    transient = max(layer.sel_ws_bytes.value, layer.bwd_ws_bytes.value, layer.fwd_ws_bytes.value)
     return dict(kept=kept, transient=transient, total=kept + transient)
 
 

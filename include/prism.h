@@ -181,11 +181,15 @@ int prism_select_blocks(const prism_problem *prob, const prism_params *par, cons
  * o           THW bf16 (out).
  * lse         float [heads][N] (out), block order: natural-log log-sum-exp
  *             of each query row's scaled scores (kept for the backward).
- * bf16 MFMA products, float32 softmax and accumulation.
+ * ws, ws_bytes  workspace (256 bytes: the work-queue counters of the
+ *             persistent kernel; size query as in prism_select_blocks).
+ * bf16 MFMA products, float32 softmax and accumulation.  Calls that share a
+ * workspace must not run concurrently.
  */
 int prism_attn_fwd(const prism_problem *prob, const prism_params *par, const prism_bf16 *qp, const prism_bf16 *kp,
                    const prism_bf16 *vp, const int32_t *perm, const int32_t *blk_start, const int32_t *n_blocks,
-                   const int32_t *row_ptr, const int32_t *col_idx, prism_bf16 *o, float *lse, prism_stream stream);
+                   const int32_t *row_ptr, const int32_t *col_idx, prism_bf16 *o, float *lse, void *ws,
+                   size_t *ws_bytes, prism_stream stream);
 
 /*
  * prism_attn_bwd -- gradients of the sparse attention with respect to Q, K
