@@ -83,8 +83,12 @@ size_t operand_bytes(const Geometry& g) { return align256(sizeof(uint16_t) * g.h
 
 size_t bwd_ws(const Geometry& g) { return operand_bytes(g) + 2 * align256(sizeof(float) * g.heads * g.N); }
 
-// work-queue counters of the persistent attention kernels
+// work-queue counters of the persistent attention kernels, and the scratch
+// of their longest-first queue order
 constexpr size_t kQueueBytes = sizeof(int) * prism::kQueueInts;
+size_t sched_bytes(const Geometry& g, bool backward) {
+  return align256(sizeof(int32_t) * (size_t)prism::sched_ints(g, backward));
+}
 
 // ---- forward-only inference path ----
 // Heads run in passes of `group` heads, enough for the attention grid to
@@ -95,7 +99,7 @@ constexpr size_t kQueueBytes = sizeof(int) * prism::kQueueInts;
 struct InferLayout {
   int group;
   int64_t lmax;  // largest possible selected blocks per query block
-  size_t zst, gv, rho, shape, perm, bs, nb, qp, kp, region, rp, col, queues, total;
+  size_t zst, gv, rho, shape, perm, bs, nb, qp, kp, region, rp, col, queues, sched, total;
 };
 
 int64_t max_row_blocks(const Geometry& g, const prism_params& p) {
@@ -132,7 +136,9 @@ InferLayout infer_layout(const Geometry& geo, const prism_params& p) {
   L.rp = align256(sizeof(int32_t) * G * (g.tiles + 1));
   L.col = align256(sizeof(int32_t) * G * g.tiles * L.lmax);
   L.queues = align256(kQueueBytes);
-  L.total = L.zst + L.gv + L.rho + L.shape + L.perm + L.bs + L.nb + L.qp + L.kp + L.region + L.rp + L.col + L.queues;
+  L.sched = sched_bytes(g, false);
+  L.total = L.zst + L.gv + L.rho + L.shape + L.perm + L.bs + L.nb + L.qp + L.kp + L.region + L.rp + L.col + L.queues +
+            L.sched;
   return L;
 }
 
@@ -228,7 +234,7 @@ int prism_attn_fwd(const prism_problem* prob, const prism_params* par, const pri
   CHECK(check_problem(prob, &geo));
   CHECK(check_params(par));
   if (!ws_bytes) return PRISM_EINVAL;
-  const size_t need = align256(kQueueBytes);
+  const size_t need = align256(kQueueBytes) + sched_bytes(geo, false);
   if (!ws) {
     *ws_bytes = need;
     return PRISM_OK;
@@ -237,7 +243,8 @@ int prism_attn_fwd(const prism_problem* prob, const prism_params* par, const pri
   if (!qp || !kp || !vp || !perm || !blk_start || !n_blocks || !row_ptr || !col_idx || !o || !lse)
     return PRISM_EINVAL;
   HIPCALL(prism::launch_attn_fwd(geo, attn_scale(*par, geo.D), qp, kp, vp, perm, blk_start, n_blocks, row_ptr,
-                                 col_idx, o, lse, (int*)ws, (hipStream_t)stream));
+                                 col_idx, o, lse, (int*)ws, (int32_t*)((char*)ws + align256(kQueueBytes)),
+                                 (hipStream_t)stream));
   return PRISM_OK;
 }
 
@@ -250,7 +257,7 @@ int prism_attn_bwd(const prism_problem* prob, const prism_params* par, const pri
   CHECK(check_problem(prob, &geo));
   CHECK(check_params(par));
   if (!ws_bytes) return PRISM_EINVAL;
-  const size_t need = bwd_ws(geo) + align256(kQueueBytes);
+  const size_t need = bwd_ws(geo) + align256(kQueueBytes) + sched_bytes(geo, true);
   if (!ws) {
     *ws_bytes = need;
     return PRISM_OK;
@@ -264,9 +271,10 @@ int prism_attn_bwd(const prism_problem* prob, const prism_params* par, const pri
   float* delta = (float*)((char*)ws + operand_bytes(geo));
   float* lse2 = (float*)((char*)delta + align256(sizeof(float) * geo.heads * geo.N));
   int* queues = (int*)((char*)ws + bwd_ws(geo));
+  int32_t* sched = (int32_t*)((char*)queues + align256(kQueueBytes));
   HIPCALL(prism::launch_bwd_pre(geo, o, dout, perm, lse, dop, delta, lse2, s));
   HIPCALL(prism::launch_attn_bwd(geo, attn_scale(*par, geo.D), qp, kp, vp, dop, lse2, delta, perm, blk_start,
-                                 n_blocks, row_ptr, col_idx, t_row_ptr, t_col_idx, dq, dk, dv, queues, s));
+                                 n_blocks, row_ptr, col_idx, t_row_ptr, t_col_idx, dq, dk, dv, queues, sched, s));
   return PRISM_OK;
 }
 
@@ -308,6 +316,7 @@ int prism_infer_fwd(const prism_problem* prob, const prism_params* par, const pr
   int32_t* rp = (int32_t*)take(L.rp);
   int32_t* col = (int32_t*)take(L.col);
   int* queues = (int*)take(L.queues);
+  int32_t* sched = (int32_t*)take(L.sched);
   uint16_t* vp = (uint16_t*)region;
 
   const float scale = attn_scale(*par, geo.D);
@@ -333,7 +342,7 @@ int prism_infer_fwd(const prism_problem* prob, const prism_params* par, const pr
                                  nullptr, nnz.data(), sel, &status, s));
     if (status != PRISM_OK) return status;
     HIPCALL(prism::launch_permute(g, v + off, perm, vp, nullptr, s));
-    HIPCALL(prism::launch_attn_fwd(g, scale, qp, kp, vp, perm, bs, nb, rp, col, o + off, nullptr, queues, s));
+    HIPCALL(prism::launch_attn_fwd(g, scale, qp, kp, vp, perm, bs, nb, rp, col, o + off, nullptr, queues, sched, s));
   }
   return PRISM_OK;
 }
@@ -361,7 +370,7 @@ int prism_dense_attn_fwd(const prism_problem* prob, const prism_params* par, con
   HIPCALL(prism::launch_permute(geo, v, nullptr, vp, nullptr, s));
   int* queues = (int*)((char*)ws + 3 * operand_bytes(geo));
   HIPCALL(prism::launch_attn_fwd(geo, attn_scale(*par, geo.D), qp, kp, vp, nullptr, nullptr, nullptr, nullptr,
-                                 nullptr, o, lse, queues, s));
+                                 nullptr, o, lse, queues, nullptr, s));
   return PRISM_OK;
 }
 
@@ -394,7 +403,7 @@ int prism_dense_attn_bwd(const prism_problem* prob, const prism_params* par, con
   int* queues = (int*)((char*)ws + 3 * ob + bwd_ws(geo));
   HIPCALL(prism::launch_bwd_pre(geo, o, dout, nullptr, lse, dop, delta, lse2, s));
   HIPCALL(prism::launch_attn_bwd(geo, attn_scale(*par, geo.D), qp, kp, vp, dop, lse2, delta, nullptr, nullptr,
-                                 nullptr, nullptr, nullptr, nullptr, nullptr, dq, dk, dv, queues, s));
+                                 nullptr, nullptr, nullptr, nullptr, nullptr, dq, dk, dv, queues, nullptr, s));
   return PRISM_OK;
 }
 

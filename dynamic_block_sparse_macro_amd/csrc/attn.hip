@@ -277,19 +277,22 @@ __device__ __forceinline__ PairIter make_iter(const Geometry& g, int h, int pair
 template <int B>
 using Parity = std::integral_constant<int, B>;
 
-// Work queues of a persistent launch: work items 0..total-1 split into 8
-// contiguous ranges, one per XCD, each with a counter in cnt[0..7] (zero at
-// launch).  A workgroup drains the queue of the XCD it runs on, then the
-// others in turn; every call on an exhausted queue moves on, so each
-// workgroup makes at most total + 8 attempts and always ends.
+// Work queues of a persistent launch: queue positions 0..total-1 split into
+// 8 contiguous ranges, one per XCD, each with a counter in cnt[0..7] (zero at
+// launch); order[pos] (NULL = identity) is the work item at a position.  A
+// workgroup drains the queue of the XCD it runs on, then the others in turn;
+// every call on an exhausted queue moves on, so each workgroup makes at most
+// total + 8 attempts and always ends.
 struct WorkQueue {
   int* cnt;
+  const int32_t* order;
   int total, per, xq, qi;
 
-  __device__ __forceinline__ void init(int* c, int n) {
+  __device__ __forceinline__ void init(int* c, const int32_t* ord, int n) {
     unsigned x;
     asm volatile("s_getreg_b32 %0, hwreg(HW_REG_XCC_ID)" : "=s"(x));
     cnt = c;
+    order = ord;
     total = n;
     per = (n + 7) / 8;
     xq = (int)(x & 7);
@@ -303,13 +306,88 @@ struct WorkQueue {
       const int hi = lo + per < total ? lo + per : total;
       if (lo < hi) {
         const int i = atomicAdd(&cnt[q], 1);
-        if (lo + i < hi) return lo + i;
+        if (lo + i < hi) return order ? order[lo + i] : lo + i;
       }
       ++qi;
     }
     return -1;
   }
 };
+
+// ---- queue order: longest work first inside each XCD's range ----
+// Cost of a work item (a pair of 64-token tiles): the key (or query) tiles
+// its lists walk, estimated as the longer of the two lists in tiles.
+
+// tiles[h][b]: sum of the sizes (in tiles) of the blocks in list b of head h
+__global__ __launch_bounds__(256) void list_tiles_kernel(const int32_t* __restrict__ blk_start,
+                                                          const int32_t* __restrict__ n_blocks,
+                                                          const int32_t* __restrict__ ptr,
+                                                          const int32_t* __restrict__ idx, int64_t tiles,
+                                                          int32_t* __restrict__ out) {
+  const int h = blockIdx.y;
+  const int b = blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  if (b >= n_blocks[h]) return;
+  const int32_t* bs = blk_start + (int64_t)h * (tiles + 1);
+  const int32_t* rp = ptr + (int64_t)h * (tiles + 1);
+  int sum = 0;
+  for (int e = rp[b] + lane; e < rp[b + 1]; e += 64) {
+    const int j = idx[e];
+    sum += bs[j + 1] - bs[j];
+  }
+  for (int o = 32; o >= 1; o >>= 1) sum += __shfl_xor(sum, o, 64);
+  if (lane == 0) out[(int64_t)h * tiles + b] = sum;
+}
+
+constexpr int kSortMax = 4096;   // largest XCD range sorted in LDS
+
+// order[pos] for the XCD range of this workgroup: positions sorted by cost
+// descending, ties by position (a bitonic sort of 64-bit keys in LDS)
+__global__ __launch_bounds__(1024) void queue_order_kernel(const int32_t* __restrict__ blk_start,
+                                                            const int32_t* __restrict__ n_blocks,
+                                                            const int32_t* __restrict__ list_tiles, int64_t tiles,
+                                                            int npair, int total, int32_t* __restrict__ order) {
+  __shared__ uint64_t key[kSortMax];
+  const int per = (total + 7) / 8;
+  const int lo = blockIdx.x * per;
+  const int hi = lo + per < total ? lo + per : total;
+  const int n = hi > lo ? hi - lo : 0;
+  int n2 = 1;
+  while (n2 < n) n2 <<= 1;
+  for (int i = threadIdx.x; i < n2; i += blockDim.x) {
+    uint64_t k = ~0ull;   // padding sorts last
+    if (i < n) {
+      const int pos = lo + i;
+      const int h = pos / npair, pair = pos % npair;
+      const int32_t* bs = blk_start + (int64_t)h * (tiles + 1);
+      const int nb = n_blocks[h];
+      const int ba = block_of_tile(bs, nb, 2 * pair);
+      const int bb = block_of_tile(bs, nb, 2 * pair + 1);
+      const int32_t* lt = list_tiles + (int64_t)h * tiles;
+      const int ca = lt[ba], cb = lt[bb];
+      const uint32_t cost = (uint32_t)(ca > cb ? ca : cb);
+      k = ((uint64_t)(0xffffffffu - cost) << 32) | (uint32_t)i;
+    }
+    key[i] = k;
+  }
+  __syncthreads();
+  for (int size = 2; size <= n2; size <<= 1)
+    for (int stride = size >> 1; stride > 0; stride >>= 1) {
+      for (int i = threadIdx.x; i < n2; i += blockDim.x) {
+        const int j = i ^ stride;
+        if (j > i) {
+          const bool up = (i & size) == 0;
+          const uint64_t a = key[i], b = key[j];
+          if ((a > b) == up) {
+            key[i] = b;
+            key[j] = a;
+          }
+        }
+      }
+      __syncthreads();
+    }
+  for (int i = threadIdx.x; i < n; i += blockDim.x) order[lo + i] = lo + (int)(uint32_t)key[i];
+}
 
 // the workgroup's next work item (uniform), -1 when all queues are empty
 __device__ __forceinline__ int fetch_work(WorkQueue& wq, int* slot) {
@@ -330,13 +408,13 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(
     Geometry g, float sl2, const uint16_t* __restrict__ qp, const uint16_t* __restrict__ kp,
     const uint16_t* __restrict__ vp, const int32_t* __restrict__ perm, const int32_t* __restrict__ blk_start,
     const int32_t* __restrict__ n_blocks, const int32_t* __restrict__ row_ptr, const int32_t* __restrict__ col_idx,
-    uint16_t* __restrict__ o, float* __restrict__ lse, int* __restrict__ cnt) {
+    uint16_t* __restrict__ o, float* __restrict__ lse, int* __restrict__ cnt, const int32_t* __restrict__ order) {
   constexpr int TB = TileGeo<D>::BYTES;
   __shared__ __attribute__((aligned(16))) char smem[2][2][TB];   // [buffer][K, V]
   __shared__ int s_work;
   const int npair = (int)(g.tiles / 2);
   WorkQueue wq;
-  wq.init(cnt, npair * g.heads);
+  wq.init(cnt, order, npair * g.heads);
   for (;;) {
   const int wk = fetch_work(wq, &s_work);
   if (wk < 0) break;
@@ -519,13 +597,13 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bwd_dq_kernel(
     const uint16_t* __restrict__ vp, const uint16_t* __restrict__ dop, const float* __restrict__ lse2,
     const float* __restrict__ delta, const int32_t* __restrict__ perm, const int32_t* __restrict__ blk_start,
     const int32_t* __restrict__ n_blocks, const int32_t* __restrict__ row_ptr, const int32_t* __restrict__ col_idx,
-    uint16_t* __restrict__ dq, int* __restrict__ cnt) {
+    uint16_t* __restrict__ dq, int* __restrict__ cnt, const int32_t* __restrict__ order) {
   constexpr int TB = TileGeo<D>::BYTES;
   __shared__ __attribute__((aligned(16))) char smem[2][2][TB];   // [buffer][K, V]
   __shared__ int s_work;
   const int npair = (int)(g.tiles / 2);
   WorkQueue wq;
-  wq.init(cnt, npair * g.heads);
+  wq.init(cnt, order, npair * g.heads);
   for (;;) {
   const int wk = fetch_work(wq, &s_work);
   if (wk < 0) break;
@@ -640,14 +718,14 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bwd_dkdv_kernel(
     const float* __restrict__ delta, const int32_t* __restrict__ perm, const int32_t* __restrict__ blk_start,
     const int32_t* __restrict__ n_blocks, const int32_t* __restrict__ t_row_ptr,
     const int32_t* __restrict__ t_col_idx, uint16_t* __restrict__ dk, uint16_t* __restrict__ dv,
-    int* __restrict__ cnt) {
+    int* __restrict__ cnt, const int32_t* __restrict__ order) {
   constexpr int TB = TileGeo<D>::BYTES;
   __shared__ __attribute__((aligned(16))) char smem[2][2][TB];   // [buffer][Q, dO]
   __shared__ __attribute__((aligned(16))) float svec[2][2][kTile]; // [buffer][lse2, delta]
   __shared__ int s_work;
   const int npair = (int)(g.tiles / 2);
   WorkQueue wq;
-  wq.init(cnt, npair * g.heads);
+  wq.init(cnt, order, npair * g.heads);
   for (;;) {
   const int wk = fetch_work(wq, &s_work);
   if (wk < 0) break;
@@ -789,17 +867,43 @@ hipError_t resident_grid(const void* kernel, unsigned* grid) {
   return hipSuccess;
 }
 
+// Queue order of a sparse launch over the lists (ptr, idx): longest work
+// first inside each XCD's range.  Returns NULL (identity order) for a dense
+// launch or when a range is too long to sort in LDS.
+hipError_t queue_order(const Geometry& g, const int32_t* blk_start, const int32_t* n_blocks, const int32_t* ptr,
+                       const int32_t* idx, int32_t* list_tiles, int32_t* order, const int32_t** out,
+                       hipStream_t s) {
+  *out = nullptr;
+  const int npair = (int)(g.tiles / 2);
+  const int total = npair * g.heads;
+  if (ptr == nullptr || order == nullptr || (total + 7) / 8 > kSortMax) return hipSuccess;
+  hipLaunchKernelGGL(list_tiles_kernel, dim3((unsigned)((g.tiles + 3) / 4), (unsigned)g.heads), dim3(256), 0, s,
+                     blk_start, n_blocks, ptr, idx, g.tiles, list_tiles);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(queue_order_kernel, dim3(8), dim3(1024), 0, s, blk_start, n_blocks, list_tiles, g.tiles, npair,
+                     total, order);
+  e = hipGetLastError();
+  if (e == hipSuccess) *out = order;
+  return e;
+}
+
 template <int D, bool DENSE>
 hipError_t fwd_impl(const Geometry& g, float scale, const uint16_t* qp, const uint16_t* kp, const uint16_t* vp,
                     const int32_t* perm, const int32_t* blk_start, const int32_t* n_blocks, const int32_t* row_ptr,
-                    const int32_t* col_idx, uint16_t* o, float* lse, int* queues, hipStream_t s) {
+                    const int32_t* col_idx, uint16_t* o, float* lse, int* queues, int32_t* sched, hipStream_t s) {
   const void* k = (const void*)attn_fwd_kernel<D, DENSE>;
   unsigned grid = 0;
   hipError_t e = resident_grid(k, &grid);
   if (e != hipSuccess) return e;
+  const int32_t* order = nullptr;
+  if (sched != nullptr) {
+    e = queue_order(g, blk_start, n_blocks, row_ptr, col_idx, sched, sched + g.heads * g.tiles, &order, s);
+    if (e != hipSuccess) return e;
+  }
   hipLaunchKernelGGL(zero_kernel, dim3(1), dim3(64), 0, s, queues, 8);
   hipLaunchKernelGGL((attn_fwd_kernel<D, DENSE>), dim3(grid), dim3(kThreads), 0, s, g, scale * kLog2e, qp, kp, vp,
-                     perm, blk_start, n_blocks, row_ptr, col_idx, o, lse, queues);
+                     perm, blk_start, n_blocks, row_ptr, col_idx, o, lse, queues, order);
   return hipGetLastError();
 }
 
@@ -808,19 +912,27 @@ hipError_t bwd_impl(const Geometry& g, float scale, const uint16_t* qp, const ui
                     const uint16_t* dop, const float* lse2, const float* delta, const int32_t* perm,
                     const int32_t* blk_start, const int32_t* n_blocks, const int32_t* row_ptr,
                     const int32_t* col_idx, const int32_t* t_row_ptr, const int32_t* t_col_idx, uint16_t* dq,
-                    uint16_t* dk, uint16_t* dv, int* queues, hipStream_t s) {
+                    uint16_t* dk, uint16_t* dv, int* queues, int32_t* sched, hipStream_t s) {
   unsigned grid_q = 0, grid_k = 0;
   hipError_t e = resident_grid((const void*)attn_bwd_dq_kernel<D, DENSE>, &grid_q);
   if (e == hipSuccess) e = resident_grid((const void*)attn_bwd_dkdv_kernel<D, DENSE>, &grid_k);
   if (e != hipSuccess) return e;
+  const int32_t *order_q = nullptr, *order_k = nullptr;
+  if (sched != nullptr) {
+    const int64_t lt = (int64_t)g.heads * g.tiles, npairs = (int64_t)g.heads * (g.tiles / 2);
+    e = queue_order(g, blk_start, n_blocks, row_ptr, col_idx, sched, sched + lt, &order_q, s);
+    if (e == hipSuccess)
+      e = queue_order(g, blk_start, n_blocks, t_row_ptr, t_col_idx, sched, sched + lt + npairs, &order_k, s);
+    if (e != hipSuccess) return e;
+  }
   hipLaunchKernelGGL(zero_kernel, dim3(1), dim3(64), 0, s, queues, 16);
   hipLaunchKernelGGL((attn_bwd_dq_kernel<D, DENSE>), dim3(grid_q), dim3(kThreads), 0, s, g, scale, scale * kLog2e, qp,
-                     kp, vp, dop, lse2, delta, perm, blk_start, n_blocks, row_ptr, col_idx, dq, queues);
+                     kp, vp, dop, lse2, delta, perm, blk_start, n_blocks, row_ptr, col_idx, dq, queues, order_q);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL((attn_bwd_dkdv_kernel<D, DENSE>), dim3(grid_k), dim3(kThreads), 0, s, g, scale, scale * kLog2e,
                      qp, kp, vp, dop, lse2, delta, perm, blk_start, n_blocks, t_row_ptr, t_col_idx, dk, dv,
-                     queues + 8);
+                     queues + 8, order_k);
   return hipGetLastError();
 }
 
@@ -829,10 +941,10 @@ hipError_t bwd_impl(const Geometry& g, float scale, const uint16_t* qp, const ui
 hipError_t launch_attn_fwd(const Geometry& g, float scale, const uint16_t* qp, const uint16_t* kp,
                            const uint16_t* vp, const int32_t* perm, const int32_t* blk_start,
                            const int32_t* n_blocks, const int32_t* row_ptr, const int32_t* col_idx, uint16_t* o,
-                           float* lse, int* queues, hipStream_t s) {
+                           float* lse, int* queues, int32_t* sched, hipStream_t s) {
   const bool dense = row_ptr == nullptr;
 #define PRISM_FWD(DD, DN) \
-  fwd_impl<DD, DN>(g, scale, qp, kp, vp, perm, blk_start, n_blocks, row_ptr, col_idx, o, lse, queues, s)
+  fwd_impl<DD, DN>(g, scale, qp, kp, vp, perm, blk_start, n_blocks, row_ptr, col_idx, o, lse, queues, sched, s)
   if (g.D == 128) return dense ? PRISM_FWD(128, true) : PRISM_FWD(128, false);
   return dense ? PRISM_FWD(64, true) : PRISM_FWD(64, false);
 #undef PRISM_FWD
@@ -853,11 +965,11 @@ hipError_t launch_attn_bwd(const Geometry& g, float scale, const uint16_t* qp, c
                            const int32_t* perm, const int32_t* blk_start, const int32_t* n_blocks,
                            const int32_t* row_ptr, const int32_t* col_idx, const int32_t* t_row_ptr,
                            const int32_t* t_col_idx, uint16_t* dq, uint16_t* dk, uint16_t* dv, int* queues,
-                           hipStream_t s) {
+                           int32_t* sched, hipStream_t s) {
   const bool dense = row_ptr == nullptr;
 #define PRISM_BWD(DD, DN)                                                                                          \
   bwd_impl<DD, DN>(g, scale, qp, kp, vp, dop, lse2, delta, perm, blk_start, n_blocks, row_ptr, col_idx, t_row_ptr, \
-                   t_col_idx, dq, dk, dv, queues, s)
+                   t_col_idx, dq, dk, dv, queues, sched, s)
   if (g.D == 128) return dense ? PRISM_BWD(128, true) : PRISM_BWD(128, false);
   return dense ? PRISM_BWD(64, true) : PRISM_BWD(64, false);
 #undef PRISM_BWD

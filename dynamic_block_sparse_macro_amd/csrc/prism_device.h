@@ -134,17 +134,4 @@ __device__ __forceinline__ int block_of_tile(const int32_t* __restrict__ bs, int
   return lo;
 }
 
-// Workgroup index remapped so that each XCD (8 per MI355X, dispatched
-// round-robin) works on a contiguous range of logical indices: neighbouring
-// query blocks, which share most of their key blocks, then share one L2.
-__device__ __forceinline__ int xcd_remap(int bid, int nblocks) {
-  const int per = (nblocks + 7) >> 3;
-  const int xcd = bid & 7, slot = bid >> 3;
-  const int full = nblocks - (per - 1) * 8;  // XCDs that get `per` workgroups
-  int logical;
-  if (xcd < full) logical = xcd * per + slot;
-  else logical = full * per + (xcd - full) * (per - 1) + slot;
-  return logical;
-}
-
 }  // namespace prism

@@ -45,12 +45,17 @@ hipError_t run_selection(const Geometry& g, const prism_params& p, const int32_t
 // ---- attention (attn.hip) ----
 // Sparse when row_ptr != NULL, dense over all tiles (64-token blocks, identity
 // perm) otherwise.  lse may be NULL (not stored).  `queues` is device scratch
-// of kQueueInts ints for the persistent work queues (cleared here, on s).
+// of kQueueInts ints for the persistent work queues (cleared here, on s);
+// `sched` (NULL: work in index order) is scratch of sched_ints(g, backward)
+// ints for the longest-first queue order.
 constexpr int kQueueInts = 64;
+inline int64_t sched_ints(const Geometry& g, bool backward) {
+  return (int64_t)g.heads * g.tiles + (backward ? 2 : 1) * (int64_t)g.heads * (g.tiles / 2);
+}
 hipError_t launch_attn_fwd(const Geometry& g, float scale, const uint16_t* qp, const uint16_t* kp,
                            const uint16_t* vp, const int32_t* perm, const int32_t* blk_start,
                            const int32_t* n_blocks, const int32_t* row_ptr, const int32_t* col_idx, uint16_t* o,
-                           float* lse, int* queues, hipStream_t s);
+                           float* lse, int* queues, int32_t* sched, hipStream_t s);
 hipError_t launch_bwd_pre(const Geometry& g, const uint16_t* o, const uint16_t* dout, const int32_t* perm,
                           const float* lse, uint16_t* dop, float* delta, float* lse2, hipStream_t s);
 hipError_t launch_attn_bwd(const Geometry& g, float scale, const uint16_t* qp, const uint16_t* kp,
@@ -58,7 +63,7 @@ hipError_t launch_attn_bwd(const Geometry& g, float scale, const uint16_t* qp, c
                            const int32_t* perm, const int32_t* blk_start, const int32_t* n_blocks,
                            const int32_t* row_ptr, const int32_t* col_idx, const int32_t* t_row_ptr,
                            const int32_t* t_col_idx, uint16_t* dq, uint16_t* dk, uint16_t* dv, int* queues,
-                           hipStream_t s);
+                           int32_t* sched, hipStream_t s);
 
 // ---- audio-to-video norm producer (a2v.hip) ----
 hipError_t launch_a2v_norms(const uint16_t* h_hat, int64_t n, int channels, int64_t stride, float* a,

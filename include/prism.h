@@ -181,8 +181,9 @@ int prism_select_blocks(const prism_problem *prob, const prism_params *par, cons
  * o           THW bf16 (out).
  * lse         float [heads][N] (out), block order: natural-log log-sum-exp
  *             of each query row's scaled scores (kept for the backward).
- * ws, ws_bytes  workspace (256 bytes: the work-queue counters of the
- *             persistent kernel; size query as in prism_select_blocks).
+ * ws, ws_bytes  workspace (the work-queue counters of the persistent
+ *             kernel and its longest-first queue order, 256 B + about 6 B per
+ *             64-token tile; size query as in prism_select_blocks).
  * bf16 MFMA products, float32 softmax and accumulation.  Calls that share a
  * workspace must not run concurrently.
  */
