@@ -69,7 +69,16 @@ struct TileGeo {
   static constexpr int ROWB = D * 2;            // bytes per row
   static constexpr int BYTES = kTile * ROWB;    // bytes per tile
   static constexpr int CHUNKS = BYTES / 16;     // 16-byte chunks per tile
+  // one pipeline stage: two operand tiles, sized to also hold the 128-row
+  // output staging area (128 x (D + 8) bf16) of the epilogue
+  static constexpr int STAGE = 2 * BYTES + 2048;
 };
+
+// The two pipeline stages are separate LDS objects (stage0, stage1) so
+// that the compiler can tell the prefetch into one stage from the reads of
+// the other; with a single array it makes every read of the current stage
+// wait for the prefetch as well, which exposes the full memory latency.
+#define PRISM_STAGE(B, s0, s1) ((B) ? (s1) : (s0))
 
 // asynchronous copy of one contiguous operand tile into LDS (all 256 threads)
 template <int D>
@@ -84,10 +93,10 @@ __device__ __forceinline__ void dma_tile(char* lds, const uint16_t* __restrict__
   }
 }
 // asynchronous copy of 64 floats (one per tile row) into LDS
-// (called by one whole wave; lanes 0..15 copy 16 bytes each)
+// (called by one whole wave; lane l copies float l)
 __device__ __forceinline__ void dma_vec64(char* lds, const float* __restrict__ src) {
   const int lane = threadIdx.x & 63;
-  if (lane < 16) __builtin_amdgcn_global_load_lds((const void*)(src + lane * 4), (lds_void*)lds, 16, 0, 0);
+  __builtin_amdgcn_global_load_lds((const void*)(src + lane), (lds_void*)lds, 4, 0, 0);
 }
 
 // Per-lane LDS byte offsets inside an operand tile.  With the XOR swizzle of
@@ -410,7 +419,8 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(
     const int32_t* __restrict__ n_blocks, const int32_t* __restrict__ row_ptr, const int32_t* __restrict__ col_idx,
     uint16_t* __restrict__ o, float* __restrict__ lse, int* __restrict__ cnt, const int32_t* __restrict__ order) {
   constexpr int TB = TileGeo<D>::BYTES;
-  __shared__ __attribute__((aligned(16))) char smem[2][2][TB];   // [buffer][K, V]
+  __shared__ __attribute__((aligned(16))) char stage0[TileGeo<D>::STAGE];   // K, V of even steps
+  __shared__ __attribute__((aligned(16))) char stage1[TileGeo<D>::STAGE];   // K, V of odd steps
   __shared__ int s_work;
   const int npair = (int)(g.tiles / 2);
   WorkQueue wq;
@@ -448,8 +458,8 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(
   bool ua, ub, ua_n = false, ub_n = false;
   bool have = it.next(kt, ua, ub);
   if (have) {
-    dma_tile<D>(smem[0][0], Kb + (int64_t)kt * kTile * D);
-    dma_tile<D>(smem[0][1], Vb + (int64_t)kt * kTile * D);
+    dma_tile<D>(stage0, Kb + (int64_t)kt * kTile * D);
+    dma_tile<D>(stage0 + TB, Vb + (int64_t)kt * kTile * D);
   }
 
   auto step = [&](auto par) {
@@ -458,12 +468,13 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(
     wait_dma();
     __syncthreads();
     if (have_next) {
-      dma_tile<D>(smem[B ^ 1][0], Kb + (int64_t)kt_next * kTile * D);
-      dma_tile<D>(smem[B ^ 1][1], Vb + (int64_t)kt_next * kTile * D);
+      char* nx = PRISM_STAGE(B ^ 1, stage0, stage1);
+      dma_tile<D>(nx, Kb + (int64_t)kt_next * kTile * D);
+      dma_tile<D>(nx + TB, Vb + (int64_t)kt_next * kTile * D);
     }
     if (second ? ub : ua) {
-      const char* Kt = smem[B][0];
-      const char* Vt = smem[B][1];
+      const char* Kt = PRISM_STAGE(B, stage0, stage1);
+      const char* Vt = Kt + TB;
       floatx16 sacc[2];
 #pragma unroll
       for (int kk = 0; kk < 2; ++kk)
@@ -542,7 +553,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(
   const float inv = 1.0f / (r_run + __shfl_xor(r_run, 32, 64));
   if (lse != nullptr && g32 == 0) lse[hN + qt * kTile + rloc] = (m_run + __log2f(l_tot)) * kLn2;
   __syncthreads();
-  uint16_t* st = (uint16_t*)&smem[0][0][0];       // 128 x (D + 8) staging rows
+  uint16_t* st = (uint16_t*)stage0;       // 128 x (D + 8) staging rows
   acc_to_stage<D>(st, oacc, 32 * w + l32, g32, inv);
   __syncthreads();
   store_pair_thw<D>(st, o, g, h, 2 * (int64_t)pair, perm);
@@ -599,7 +610,8 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bwd_dq_kernel(
     const int32_t* __restrict__ n_blocks, const int32_t* __restrict__ row_ptr, const int32_t* __restrict__ col_idx,
     uint16_t* __restrict__ dq, int* __restrict__ cnt, const int32_t* __restrict__ order) {
   constexpr int TB = TileGeo<D>::BYTES;
-  __shared__ __attribute__((aligned(16))) char smem[2][2][TB];   // [buffer][K, V]
+  __shared__ __attribute__((aligned(16))) char stage0[TileGeo<D>::STAGE];   // K, V of even steps
+  __shared__ __attribute__((aligned(16))) char stage1[TileGeo<D>::STAGE];   // K, V of odd steps
   __shared__ int s_work;
   const int npair = (int)(g.tiles / 2);
   WorkQueue wq;
@@ -647,8 +659,8 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bwd_dq_kernel(
   bool ua, ub, ua_n = false, ub_n = false;
   bool have = it.next(kt, ua, ub);
   if (have) {
-    dma_tile<D>(smem[0][0], Kb + (int64_t)kt * kTile * D);
-    dma_tile<D>(smem[0][1], Vb + (int64_t)kt * kTile * D);
+    dma_tile<D>(stage0, Kb + (int64_t)kt * kTile * D);
+    dma_tile<D>(stage0 + TB, Vb + (int64_t)kt * kTile * D);
   }
   auto step = [&](auto par) {
     constexpr int B = decltype(par)::value;
@@ -656,12 +668,13 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bwd_dq_kernel(
     wait_dma();
     __syncthreads();
     if (have_next) {
-      dma_tile<D>(smem[B ^ 1][0], Kb + (int64_t)kt_next * kTile * D);
-      dma_tile<D>(smem[B ^ 1][1], Vb + (int64_t)kt_next * kTile * D);
+      char* nx = PRISM_STAGE(B ^ 1, stage0, stage1);
+      dma_tile<D>(nx, Kb + (int64_t)kt_next * kTile * D);
+      dma_tile<D>(nx + TB, Vb + (int64_t)kt_next * kTile * D);
     }
     if (second ? ub : ua) {
-      const char* Kt = smem[B][0];
-      const char* Vt = smem[B][1];
+      const char* Kt = PRISM_STAGE(B, stage0, stage1);
+      const char* Vt = Kt + TB;
 #pragma unroll
       for (int kk = 0; kk < 2; ++kk) {
         floatx16 sacc, pacc = ndelta;
@@ -700,7 +713,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bwd_dq_kernel(
     step(Parity<1>{});
   }
   __syncthreads();
-  uint16_t* st = (uint16_t*)&smem[0][0][0];
+  uint16_t* st = (uint16_t*)stage0;
   acc_to_stage<D>(st, dqacc, 32 * w + l32, g32, scale);
   __syncthreads();
   store_pair_thw<D>(st, dq, g, h, 2 * (int64_t)pair, perm);
@@ -720,8 +733,9 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bwd_dkdv_kernel(
     const int32_t* __restrict__ t_col_idx, uint16_t* __restrict__ dk, uint16_t* __restrict__ dv,
     int* __restrict__ cnt, const int32_t* __restrict__ order) {
   constexpr int TB = TileGeo<D>::BYTES;
-  __shared__ __attribute__((aligned(16))) char smem[2][2][TB];   // [buffer][Q, dO]
-  __shared__ __attribute__((aligned(16))) float svec[2][2][kTile]; // [buffer][lse2, delta]
+  // Q, dO, then lse2 and delta (64 floats each) of even / odd steps
+  __shared__ __attribute__((aligned(16))) char stage0[TileGeo<D>::STAGE];
+  __shared__ __attribute__((aligned(16))) char stage1[TileGeo<D>::STAGE];
   __shared__ int s_work;
   const int npair = (int)(g.tiles / 2);
   WorkQueue wq;
@@ -761,48 +775,57 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bwd_dkdv_kernel(
   int qt, qt_next = 0;
   bool ua, ub, ua_n = false, ub_n = false;
   bool have = it.next(qt, ua, ub);
-  auto issue = [&](int b, int tq) {
-    dma_tile<D>(smem[b][0], Qb + (int64_t)tq * kTile * D);
-    dma_tile<D>(smem[b][1], Db + (int64_t)tq * kTile * D);
-    if (w == 0) dma_vec64((char*)svec[b][0], lse2 + hN + (int64_t)tq * kTile);
-    if (w == 1) dma_vec64((char*)svec[b][1], delta + hN + (int64_t)tq * kTile);
+  auto issue = [&](auto par, int tq) {
+    constexpr int B = decltype(par)::value;
+    char* st = PRISM_STAGE(B, stage0, stage1);
+    dma_tile<D>(st, Qb + (int64_t)tq * kTile * D);
+    dma_tile<D>(st + TB, Db + (int64_t)tq * kTile * D);
+    // even waves copy lse2, odd waves delta (each copy is made twice, with
+    // equal values; no branch around the copy)
+    dma_vec64(st + 2 * TB + (w & 1) * 4 * kTile, ((w & 1) ? delta : lse2) + hN + (int64_t)tq * kTile);
   };
-  if (have) issue(0, qt);
+  if (have) issue(Parity<0>{}, qt);
   auto step = [&](auto par) {
     constexpr int B = decltype(par)::value;
     const bool have_next = it.next(qt_next, ua_n, ub_n);
     wait_dma();
     __syncthreads();
-    if (have_next) issue(B ^ 1, qt_next);
+    if (have_next) issue(Parity<B ^ 1>{}, qt_next);
     if (second ? ub : ua) {
-      const char* Qt = smem[B][0];
-      const char* Dt = smem[B][1];
+      const char* Qt = PRISM_STAGE(B, stage0, stage1);
+      const char* Dt = Qt + TB;
+      const float* sl = (const float*)(Qt + 2 * TB);     // lse2
+      const float* sd = sl + kTile;                         // delta
+      // S and dP of both 32-query halves first: the MFMAs of the second half
+      // then run while the first half's softmax VALU work issues
+      floatx16 sacc[2], pacc[2];
 #pragma unroll
       for (int qq = 0; qq < 2; ++qq) {
-        // all LDS operands of this half first, so their latency overlaps the MFMAs
         bf16x8 qa[D / 16], da[D / 16];
 #pragma unroll
         for (int s = 0; s < D / 16; ++s) {
           qa[s] = lds_row<D>(Qt, off, qq, s);
           da[s] = lds_row<D>(Dt, off, qq, s);
         }
-        floatx16 sacc, pacc;
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
           // dP starts at -delta of each query row (rows 32 qq + 8 j + 4 g + e)
-          const float4 d4 = *(const float4*)(&svec[B][1][32 * qq + 8 * j + 4 * g32]);
-          pacc[4 * j] = d4.x;
-          pacc[4 * j + 1] = d4.y;
-          pacc[4 * j + 2] = d4.z;
-          pacc[4 * j + 3] = d4.w;
+          const float4 d4 = *(const float4*)(&sd[32 * qq + 8 * j + 4 * g32]);
+          pacc[qq][4 * j] = d4.x;
+          pacc[qq][4 * j + 1] = d4.y;
+          pacc[qq][4 * j + 2] = d4.z;
+          pacc[qq][4 * j + 3] = d4.w;
         }
 #pragma unroll
-        for (int i = 0; i < 16; ++i) sacc[i] = 0.0f;
+        for (int i = 0; i < 16; ++i) sacc[qq][i] = 0.0f;
 #pragma unroll
         for (int s = 0; s < D / 16; ++s) {
-          sacc = mfma32(qa[s], kreg[s], sacc);
-          pacc = mfma32(da[s], vreg[s], pacc);   // dP - delta
+          sacc[qq] = mfma32(qa[s], kreg[s], sacc[qq]);
+          pacc[qq] = mfma32(da[s], vreg[s], pacc[qq]);   // dP - delta
         }
+      }
+#pragma unroll
+      for (int qq = 0; qq < 2; ++qq) {
         bf16x8 dta[2][D / 32], qta[2][D / 32];
 #pragma unroll
         for (int hh = 0; hh < 2; ++hh)
@@ -814,14 +837,14 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bwd_dkdv_kernel(
         bf16x8 pb[2], dsb[2];
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-          const float4 l4 = *(const float4*)(&svec[B][0][32 * qq + 8 * j + 4 * g32]);
+          const float4 l4 = *(const float4*)(&sl[32 * qq + 8 * j + 4 * g32]);
           const float lv[4] = {l4.x, l4.y, l4.z, l4.w};
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
             const int i = 4 * j + e;
-            const float pv = fast_exp2(__builtin_fmaf(sacc[i], sl2, -lv[e]));
+            const float pv = fast_exp2(__builtin_fmaf(sacc[qq][i], sl2, -lv[e]));
             pb[i >> 3][i & 7] = (__bf16)pv;
-            dsb[i >> 3][i & 7] = (__bf16)(pv * pacc[i]);
+            dsb[i >> 3][i & 7] = (__bf16)(pv * pacc[qq][i]);
           }
         }
 #pragma unroll
@@ -843,7 +866,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bwd_dkdv_kernel(
     if (!have) break;
     step(Parity<1>{});
   }
-  uint16_t* st = (uint16_t*)&smem[0][0][0];
+  uint16_t* st = (uint16_t*)stage0;
   __syncthreads();
   acc_to_stage<D>(st, dkacc, 32 * w + l32, g32, scale);
   __syncthreads();
