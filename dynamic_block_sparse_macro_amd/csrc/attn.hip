@@ -823,6 +823,8 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bwd_dkdv_kernel(
           sacc[qq] = mfma32(qa[s], kreg[s], sacc[qq]);
           pacc[qq] = mfma32(da[s], vreg[s], pacc[qq]);   // dP - delta
         }
+        __builtin_amdgcn_sched_group_barrier(0x100, D / 8, 0);   // this half's row reads first
+        __builtin_amdgcn_sched_group_barrier(0x008, D / 8, 0);   // then its S and dP MFMAs
       }
 #pragma unroll
       for (int qq = 0; qq < 2; ++qq) {
