@@ -18,8 +18,9 @@
 //    (S^T = K Q^T, O^T = V^T P^T, ...) so that the accumulator of one product
 //    is, register for register, the B operand of the next;
 //  * operand tiles live in HBM exactly as they sit in LDS (row-major, XOR
-//    swizzled 16-byte chunks), so staging is an asynchronous global->LDS copy
-//    (global_load_lds_dwordx4), double-buffered behind the MFMA work;
+//    swizzled 16-byte chunks), so staging is an asynchronous copy into LDS
+//    (buffer_load_dwordx4 ... lds, addressed from scalar registers),
+//    double-buffered behind the MFMA work;
 //  * operands that need a tile's columns (V^T, K^T, Q^T, dO^T) are read from
 //    the same row tiles with the transposing LDS read ds_read_b64_tr_b16;
 //  * float32 online softmax in the log2 domain with lazy rescaling (the
@@ -80,23 +81,31 @@ struct TileGeo {
 // wait for the prefetch as well, which exposes the full memory latency.
 #define PRISM_STAGE(B, s0, s1) ((B) ? (s1) : (s0))
 
+// Copies into LDS go through buffer loads: the copy's base address sits in
+// a scalar buffer descriptor (record count = the copy's size), the per-lane
+// offset is a loop-invariant vector register and the wave's part of the
+// offset a scalar, and M0 (the LDS address) is scalar too, so a copy costs
+// no vector ALU work.
+constexpr int kRsrcFlags = 0x00020000;   // descriptor word 3: 32-bit data format
+
 // asynchronous copy of one contiguous operand tile into LDS (all 256 threads)
 template <int D>
 __device__ __forceinline__ void dma_tile(char* lds, const uint16_t* __restrict__ src) {
-  const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const char* s = (const char*)src;
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
+  const __amdgpu_buffer_rsrc_t r =
+      __builtin_amdgcn_make_buffer_rsrc((void*)src, (short)0, TileGeo<D>::BYTES, kRsrcFlags);
 #pragma unroll
   for (int it = 0; it < TileGeo<D>::CHUNKS / kThreads; ++it) {
     const int chunk0 = it * kThreads + w * 64;
-    __builtin_amdgcn_global_load_lds((const void*)(s + (chunk0 + lane) * 16), (lds_void*)(lds + chunk0 * 16), 16, 0,
-                                     0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)(lds + chunk0 * 16), 16, lane * 16, chunk0 * 16, 0, 0);
   }
 }
 // asynchronous copy of 64 floats (one per tile row) into LDS
 // (called by one whole wave; lane l copies float l)
 __device__ __forceinline__ void dma_vec64(char* lds, const float* __restrict__ src) {
   const int lane = threadIdx.x & 63;
-  __builtin_amdgcn_global_load_lds((const void*)(src + lane), (lds_void*)lds, 4, 0, 0);
+  const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc((void*)src, (short)0, 64 * 4, kRsrcFlags);
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)lds, 4, lane * 4, 0, 0, 0);
 }
 
 // Per-lane LDS byte offsets inside an operand tile.  With the XOR swizzle of
@@ -402,7 +411,7 @@ __global__ __launch_bounds__(1024) void queue_order_kernel(const int32_t* __rest
 __device__ __forceinline__ int fetch_work(WorkQueue& wq, int* slot) {
   if (threadIdx.x == 0) *slot = wq.next();
   __syncthreads();
-  return *slot;
+  return __builtin_amdgcn_readfirstlane(*slot);   // uniform: scalar registers from here on
 }
 
 __global__ void zero_kernel(int* __restrict__ p, int n) {
@@ -430,7 +439,8 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(
   if (wk < 0) break;
   const int h = wk / npair;
   const int pair = wk % npair;
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, g32 = lane >> 5, l32 = lane & 31;
+  const int lane = threadIdx.x & 63, g32 = lane >> 5, l32 = lane & 31;
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // wave index, uniform
   const bool second = w >= 2;
   const int64_t hN = (int64_t)h * g.N;
   const int64_t qt = 2 * pair + (second ? 1 : 0);
@@ -621,7 +631,8 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bwd_dq_kernel(
   if (wk < 0) break;
   const int h = wk / npair;
   const int pair = wk % npair;
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, g32 = lane >> 5, l32 = lane & 31;
+  const int lane = threadIdx.x & 63, g32 = lane >> 5, l32 = lane & 31;
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // wave index, uniform
   const bool second = w >= 2;
   const int64_t hN = (int64_t)h * g.N;
   const int64_t qt = 2 * pair + (second ? 1 : 0);
@@ -745,7 +756,8 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bwd_dkdv_kernel(
   if (wk < 0) break;
   const int h = wk / npair;
   const int pair = wk % npair;
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, g32 = lane >> 5, l32 = lane & 31;
+  const int lane = threadIdx.x & 63, g32 = lane >> 5, l32 = lane & 31;
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // wave index, uniform
   const bool second = w >= 2;
   const int64_t hN = (int64_t)h * g.N;
   const int64_t kt = 2 * pair + (second ? 1 : 0);
