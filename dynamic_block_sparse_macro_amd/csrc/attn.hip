@@ -808,17 +808,29 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bwd_dkdv_kernel(
       const char* Dt = Qt + TB;
       const float* sl = (const float*)(Qt + 2 * TB);     // lse2
       const float* sd = sl + kTile;                         // delta
-      // S and dP of both 32-query halves first: the MFMAs of the second half
-      // then run while the first half's softmax VALU work issues
+      // Software pipeline over the two 32-query halves h0, h1 of the tile:
+      //   A: S, dP of h0 while the row operands of h1 load;
+      //   B: S, dP of h1 while the column operands of h0 load and h0's
+      //      softmax (P, dS) runs;
+      //   C: dV, dK of h0 while the column operands of h1 load and h1's
+      //      softmax runs;
+      //   D: dV, dK of h1 (still in flight when the next step starts).
+      // Each phase is written as chunks of one matrix product plus its share
+      // of loads and vector work, fenced by scheduling barriers, so that the
+      // products issue evenly between the other instructions (one wave per
+      // SIMD here: nothing else hides a gap in the matrix pipe).
       floatx16 sacc[2], pacc[2];
-#pragma unroll
-      for (int qq = 0; qq < 2; ++qq) {
-        bf16x8 qa[D / 16], da[D / 16];
+      bf16x8 qa[2][D / 16], da[2][D / 16];
+      bf16x8 dta[2][2][D / 32], qta[2][2][D / 32];
+      bf16x8 pb[2][2], dsb[2][2];
+      auto rows = [&](int qq) {
 #pragma unroll
         for (int s = 0; s < D / 16; ++s) {
-          qa[s] = lds_row<D>(Qt, off, qq, s);
-          da[s] = lds_row<D>(Dt, off, qq, s);
+          qa[qq][s] = lds_row<D>(Qt, off, qq, s);
+          da[qq][s] = lds_row<D>(Dt, off, qq, s);
         }
+      };
+      auto seed = [&](int qq) {
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
           // dP starts at -delta of each query row (rows 32 qq + 8 j + 4 g + e)
@@ -830,45 +842,91 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bwd_dkdv_kernel(
         }
 #pragma unroll
         for (int i = 0; i < 16; ++i) sacc[qq][i] = 0.0f;
-#pragma unroll
-        for (int s = 0; s < D / 16; ++s) {
-          sacc[qq] = mfma32(qa[s], kreg[s], sacc[qq]);
-          pacc[qq] = mfma32(da[s], vreg[s], pacc[qq]);   // dP - delta
-        }
-        __builtin_amdgcn_sched_group_barrier(0x100, D / 8, 0);   // this half's row reads first
-        __builtin_amdgcn_sched_group_barrier(0x008, D / 8, 0);   // then its S and dP MFMAs
-      }
-#pragma unroll
-      for (int qq = 0; qq < 2; ++qq) {
-        bf16x8 dta[2][D / 32], qta[2][D / 32];
-#pragma unroll
-        for (int hh = 0; hh < 2; ++hh)
-#pragma unroll
-          for (int u = 0; u < D / 32; ++u) {
-            dta[hh][u] = lds_col<D>(Dt, off, u, qq, hh);
-            qta[hh][u] = lds_col<D>(Qt, off, u, qq, hh);
-          }
-        bf16x8 pb[2], dsb[2];
+      };
+      constexpr int NM = D / 8;   // products per phase (one per chunk)
+      // one matrix product of a phase: S (even m) or dP (odd m) of half qq
+      auto sdp1 = [&](int qq, int m) {
+        const int s = m >> 1;
+        if (m & 1) pacc[qq] = mfma32(da[qq][s], vreg[s], pacc[qq]);   // dP - delta
+        else sacc[qq] = mfma32(qa[qq][s], kreg[s], sacc[qq]);
+      };
+      auto row1 = [&](int qq, int m) {
+        const int s = m >> 1;
+        if (m & 1) da[qq][s] = lds_row<D>(Dt, off, qq, s);
+        else qa[qq][s] = lds_row<D>(Qt, off, qq, s);
+      };
+      // product m of dV (even) / dK (odd) for half qq, and the column load it needs
+      auto dvdk1 = [&](int qq, int m) {
+        const int hh = (m >> 1) / (D / 32), u = (m >> 1) % (D / 32);
+        if (m & 1) dkacc[u] = mfma32(qta[qq][hh][u], dsb[qq][hh], dkacc[u]);
+        else dvacc[u] = mfma32(dta[qq][hh][u], pb[qq][hh], dvacc[u]);
+      };
+      auto col1 = [&](int qq, int m) {
+        const int hh = (m >> 1) / (D / 32), u = (m >> 1) % (D / 32);
+        if (m & 1) qta[qq][hh][u] = lds_col<D>(Qt, off, u, qq, hh);
+        else dta[qq][hh][u] = lds_col<D>(Dt, off, u, qq, hh);
+      };
+      float lv[16];
+      auto lse_load = [&](int qq) {
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
           const float4 l4 = *(const float4*)(&sl[32 * qq + 8 * j + 4 * g32]);
-          const float lv[4] = {l4.x, l4.y, l4.z, l4.w};
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const int i = 4 * j + e;
-            const float pv = fast_exp2(__builtin_fmaf(sacc[qq][i], sl2, -lv[e]));
-            pb[i >> 3][i & 7] = (__bf16)pv;
-            dsb[i >> 3][i & 7] = (__bf16)(pv * pacc[qq][i]);
-          }
+          lv[4 * j] = l4.x;
+          lv[4 * j + 1] = l4.y;
+          lv[4 * j + 2] = l4.z;
+          lv[4 * j + 3] = l4.w;
         }
+      };
+      // P and dS of elements i, i + 1 of half qq
+      auto soft2 = [&](int qq, int i) {
 #pragma unroll
-        for (int hh = 0; hh < 2; ++hh)
+        for (int e = i; e < i + 2; ++e) {
+          const float pv = fast_exp2(__builtin_fmaf(sacc[qq][e], sl2, -lv[e]));
+          pb[qq][e >> 3][e & 7] = (__bf16)pv;
+          dsb[qq][e >> 3][e & 7] = (__bf16)(pv * pacc[qq][e]);
+        }
+      };
+      // softmax pairs of chunk m: 8 pairs over NM chunks
+      auto soft_chunk = [&](int qq, int m) {
+        if constexpr (NM >= 8) {
+          if ((m % (NM / 8)) == NM / 8 - 1) soft2(qq, 2 * (m / (NM / 8)));
+        } else {
 #pragma unroll
-          for (int u = 0; u < D / 32; ++u) {
-            dvacc[u] = mfma32(dta[hh][u], pb[hh], dvacc[u]);
-            dkacc[u] = mfma32(qta[hh][u], dsb[hh], dkacc[u]);
-          }
+          for (int p = 0; p < 8 / NM; ++p) soft2(qq, 2 * (m * (8 / NM) + p));
+        }
+      };
+      // A: S, dP of h0; row loads of h1
+      rows(0);
+      seed(0);
+      seed(1);
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int m = 0; m < NM; ++m) {
+        sdp1(0, m);
+        row1(1, m);
+        __builtin_amdgcn_sched_barrier(0);
       }
+      // B: S, dP of h1; column loads and softmax of h0
+      lse_load(0);
+#pragma unroll
+      for (int m = 0; m < NM; ++m) {
+        sdp1(1, m);
+        col1(0, m);
+        soft_chunk(0, m);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      // C: dV, dK of h0; column loads and softmax of h1
+      lse_load(1);
+#pragma unroll
+      for (int m = 0; m < NM; ++m) {
+        dvdk1(0, m);
+        col1(1, m);
+        soft_chunk(1, m);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      // D: dV, dK of h1
+#pragma unroll
+      for (int m = 0; m < NM; ++m) dvdk1(1, m);
     }
     qt = qt_next;
     ua = ua_n;
