@@ -191,6 +191,20 @@ __device__ __forceinline__ void store_pair_thw(const uint16_t* st, uint16_t* __r
   }
 }
 
+// the same for two tiles anywhere in the head: staged rows 0..63 are tile
+// ta, rows 64..127 tile tb
+template <int D>
+__device__ __forceinline__ void store_tiles_thw(const uint16_t* st, uint16_t* __restrict__ out, const Geometry& g,
+                                                int h, int64_t ta, int64_t tb, const int32_t* __restrict__ perm) {
+  constexpr int CH = D / 8, LD = D + 8;
+  for (int c = threadIdx.x; c < 2 * kTile * CH; c += kThreads) {
+    const int r = c / CH, k = c % CH;
+    const int64_t p = (r < kTile ? ta : tb) * kTile + (r & (kTile - 1));
+    const int64_t n = perm ? (int64_t)perm[(int64_t)h * g.N + p] : p;
+    *(uint4*)(out + (int64_t)h * g.hstride + n * g.tstride + k * 8) = *(const uint4*)(st + r * LD + k * 8);
+  }
+}
+
 // A window on an ascending block list: lane i holds entry base + i (block
 // index and its tile range, loaded together), so the iterator reads the next
 // block with a lane read instead of two dependent memory round trips, and
@@ -257,8 +271,8 @@ struct PairIter {
   }
 };
 
-// the key (or query) lists of the two tiles of pair `pair` for head h
-__device__ __forceinline__ PairIter make_iter(const Geometry& g, int h, int pair, const int32_t* __restrict__ blk_start,
+// the key (or query) lists of tiles ta and tb (a work item's two tiles) of head h
+__device__ __forceinline__ PairIter make_iter(const Geometry& g, int h, int ta, int tb, const int32_t* __restrict__ blk_start,
                                               const int32_t* __restrict__ n_blocks,
                                               const int32_t* __restrict__ ptr, const int32_t* __restrict__ idx) {
   PairIter it;
@@ -276,8 +290,8 @@ __device__ __forceinline__ PairIter make_iter(const Geometry& g, int h, int pair
   it.dense = false;
   const int32_t* bs = blk_start + (int64_t)h * (g.tiles + 1);
   const int nbk = n_blocks[h];
-  const int ba = block_of_tile(bs, nbk, 2 * pair);
-  const int bb = block_of_tile(bs, nbk, 2 * pair + 1);
+  const int ba = block_of_tile(bs, nbk, ta);
+  const int bb = block_of_tile(bs, nbk, tb);
   const int32_t* rp = ptr + (int64_t)h * (g.tiles + 1);
   it.bs = bs;
   it.same = ba == bb;
@@ -357,13 +371,87 @@ __global__ __launch_bounds__(256) void list_tiles_kernel(const int32_t* __restri
   if (lane == 0) out[(int64_t)h * tiles + b] = sum;
 }
 
+// Tile-weighted size of the intersection of the lists of blocks ba and bb
+// (ascending block indices): one wave, every lane gets the sum.
+__device__ __forceinline__ int list_overlap(const int32_t* __restrict__ bs, const int32_t* __restrict__ rp,
+                                            const int32_t* __restrict__ idx, int ba, int bb) {
+  const int lane = threadIdx.x & 63;
+  const int32_t* B = idx + rp[bb];
+  const int nB = rp[bb + 1] - rp[bb];
+  int sum = 0;
+  for (int e = rp[ba] + lane; e < rp[ba + 1]; e += 64) {
+    const int j = idx[e];
+    int lo = 0, hi = nB;   // first position with B[pos] >= j
+    while (lo < hi) {
+      const int mid = (lo + hi) >> 1;
+      if (B[mid] < j) lo = mid + 1; else hi = mid;
+    }
+    if (lo < nB && B[lo] == j) sum += bs[j + 1] - bs[j];
+  }
+  for (int o = 32; o >= 1; o >>= 1) sum += __shfl_xor(sum, o, 64);
+  return sum;
+}
+
+// Key-tile pairs of the key-major pass, one wave per 8-tile zone.  A zone of
+// eight one-tile blocks (volume 64) pairs its tiles either as (2i, 2i + 1)
+// or as (i, i + 4), whichever walks fewer union steps: the two tiles of a
+// pair share a work item, so the query tiles in one list but not the other
+// leave half of the workgroup idle.  Other zones keep (2i, 2i + 1), which
+// lie in one block and share its list.  pairs[h][p] = (ta, tb); cost[h][p] =
+// the union's length in tiles.
+__global__ __launch_bounds__(64) void key_pairs_kernel(const int32_t* __restrict__ blk_start,
+                                                       const int32_t* __restrict__ n_blocks,
+                                                       const int32_t* __restrict__ ptr,
+                                                       const int32_t* __restrict__ idx,
+                                                       const int32_t* __restrict__ list_tiles, int64_t tiles,
+                                                       int32_t* __restrict__ pairs, int32_t* __restrict__ cost) {
+  const int h = blockIdx.y;
+  const int t0 = blockIdx.x * 8;
+  const int lane = threadIdx.x;
+  const int32_t* bs = blk_start + (int64_t)h * (tiles + 1);
+  const int32_t* rp = ptr + (int64_t)h * (tiles + 1);
+  const int32_t* lt = list_tiles + (int64_t)h * tiles;
+  const int nb = n_blocks[h];
+  const int b0 = block_of_tile(bs, nb, t0);
+  const bool single = block_of_tile(bs, nb, t0 + 7) - b0 == 7;
+  auto uni = [&](int ta, int tb) {
+    const int ba = single ? b0 + ta : block_of_tile(bs, nb, t0 + ta);
+    const int bb = single ? b0 + tb : block_of_tile(bs, nb, t0 + tb);
+    return ba == bb ? lt[ba] : lt[ba] + lt[bb] - list_overlap(bs, rp, idx, ba, bb);
+  };
+  int u[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) u[i] = uni(2 * i, 2 * i + 1);
+  int stride = 1;
+  if (single) {
+    int u4[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) u4[i] = uni(i, i + 4);
+    if (u4[0] + u4[1] + u4[2] + u4[3] < u[0] + u[1] + u[2] + u[3]) {
+      stride = 4;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) u[i] = u4[i];
+    }
+  }
+  if (lane < 4) {
+    const int64_t p = (int64_t)h * (tiles / 2) + t0 / 2 + lane;
+    const int ta = stride == 1 ? 2 * lane : lane;
+    pairs[2 * p] = t0 + ta;
+    pairs[2 * p + 1] = t0 + ta + stride;
+    cost[p] = lane == 0 ? u[0] : lane == 1 ? u[1] : lane == 2 ? u[2] : u[3];
+  }
+}
+
 constexpr int kSortMax = 4096;   // largest XCD range sorted in LDS
 
 // order[pos] for the XCD range of this workgroup: positions sorted by cost
-// descending, ties by position (a bitonic sort of 64-bit keys in LDS)
+// descending, ties by position (a bitonic sort of 64-bit keys in LDS).  The
+// cost of a position is pair_cost[pos] when given, else the longer list of
+// its tiles (2 pair, 2 pair + 1).
 __global__ __launch_bounds__(1024) void queue_order_kernel(const int32_t* __restrict__ blk_start,
                                                             const int32_t* __restrict__ n_blocks,
-                                                            const int32_t* __restrict__ list_tiles, int64_t tiles,
+                                                            const int32_t* __restrict__ list_tiles,
+                                                            const int32_t* __restrict__ pair_cost, int64_t tiles,
                                                             int npair, int total, int32_t* __restrict__ order) {
   __shared__ uint64_t key[kSortMax];
   const int per = (total + 7) / 8;
@@ -376,14 +464,19 @@ __global__ __launch_bounds__(1024) void queue_order_kernel(const int32_t* __rest
     uint64_t k = ~0ull;   // padding sorts last
     if (i < n) {
       const int pos = lo + i;
-      const int h = pos / npair, pair = pos % npair;
-      const int32_t* bs = blk_start + (int64_t)h * (tiles + 1);
-      const int nb = n_blocks[h];
-      const int ba = block_of_tile(bs, nb, 2 * pair);
-      const int bb = block_of_tile(bs, nb, 2 * pair + 1);
-      const int32_t* lt = list_tiles + (int64_t)h * tiles;
-      const int ca = lt[ba], cb = lt[bb];
-      const uint32_t cost = (uint32_t)(ca > cb ? ca : cb);
+      uint32_t cost;
+      if (pair_cost != nullptr) {
+        cost = (uint32_t)pair_cost[pos];
+      } else {
+        const int h = pos / npair, pair = pos % npair;
+        const int32_t* bs = blk_start + (int64_t)h * (tiles + 1);
+        const int nb = n_blocks[h];
+        const int ba = block_of_tile(bs, nb, 2 * pair);
+        const int bb = block_of_tile(bs, nb, 2 * pair + 1);
+        const int32_t* lt = list_tiles + (int64_t)h * tiles;
+        const int ca = lt[ba], cb = lt[bb];
+        cost = (uint32_t)(ca > cb ? ca : cb);
+      }
       k = ((uint64_t)(0xffffffffu - cost) << 32) | (uint32_t)i;
     }
     key[i] = k;
@@ -463,7 +556,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(
     for (int i = 0; i < 16; ++i) oacc[u][i] = 0.0f;
   float m_run = -INFINITY, l_run = 0.0f, r_run = 0.0f;
 
-  PairIter it = make_iter(g, h, pair, blk_start, n_blocks, DENSE ? nullptr : row_ptr, col_idx);
+  PairIter it = make_iter(g, h, 2 * pair, 2 * pair + 1, blk_start, n_blocks, DENSE ? nullptr : row_ptr, col_idx);
   int kt, kt_next = 0;
   bool ua, ub, ua_n = false, ub_n = false;
   bool have = it.next(kt, ua, ub);
@@ -665,7 +758,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bwd_dq_kernel(
 #pragma unroll
     for (int i = 0; i < 16; ++i) dqacc[u][i] = 0.0f;
 
-  PairIter it = make_iter(g, h, pair, blk_start, n_blocks, DENSE ? nullptr : row_ptr, col_idx);
+  PairIter it = make_iter(g, h, 2 * pair, 2 * pair + 1, blk_start, n_blocks, DENSE ? nullptr : row_ptr, col_idx);
   int kt, kt_next = 0;
   bool ua, ub, ua_n = false, ub_n = false;
   bool have = it.next(kt, ua, ub);
@@ -742,7 +835,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bwd_dkdv_kernel(
     const float* __restrict__ delta, const int32_t* __restrict__ perm, const int32_t* __restrict__ blk_start,
     const int32_t* __restrict__ n_blocks, const int32_t* __restrict__ t_row_ptr,
     const int32_t* __restrict__ t_col_idx, uint16_t* __restrict__ dk, uint16_t* __restrict__ dv,
-    int* __restrict__ cnt, const int32_t* __restrict__ order) {
+    int* __restrict__ cnt, const int32_t* __restrict__ order, const int32_t* __restrict__ pairs) {
   constexpr int TB = TileGeo<D>::BYTES;
   // Q, dO, then lse2 and delta (64 floats each) of even / odd steps
   __shared__ __attribute__((aligned(16))) char stage0[TileGeo<D>::STAGE];
@@ -760,7 +853,13 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bwd_dkdv_kernel(
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // wave index, uniform
   const bool second = w >= 2;
   const int64_t hN = (int64_t)h * g.N;
-  const int64_t kt = 2 * pair + (second ? 1 : 0);
+  // the work item's key tiles: (2 pair, 2 pair + 1) or the pair table's
+  int ta = 2 * pair, tb = 2 * pair + 1;
+  if (!DENSE && pairs != nullptr) {
+    ta = pairs[2 * ((int64_t)h * npair + pair)];
+    tb = pairs[2 * ((int64_t)h * npair + pair) + 1];
+  }
+  const int64_t kt = second ? tb : ta;
   const int rloc = 32 * (w & 1) + l32;
   const uint16_t* Qb = qp + hN * D;
   const uint16_t* Db = dop + hN * D;
@@ -783,7 +882,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bwd_dkdv_kernel(
 #pragma unroll
     for (int i = 0; i < 16; ++i) dkacc[u][i] = dvacc[u][i] = 0.0f;
 
-  PairIter it = make_iter(g, h, pair, blk_start, n_blocks, DENSE ? nullptr : t_row_ptr, t_col_idx);
+  PairIter it = make_iter(g, h, ta, tb, blk_start, n_blocks, DENSE ? nullptr : t_row_ptr, t_col_idx);
   int qt, qt_next = 0;
   bool ua, ub, ua_n = false, ub_n = false;
   bool have = it.next(qt, ua, ub);
@@ -942,11 +1041,11 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bwd_dkdv_kernel(
   __syncthreads();
   acc_to_stage<D>(st, dkacc, 32 * w + l32, g32, scale);
   __syncthreads();
-  store_pair_thw<D>(st, dk, g, h, 2 * (int64_t)pair, perm);
+  store_tiles_thw<D>(st, dk, g, h, ta, tb, perm);
   __syncthreads();
   acc_to_stage<D>(st, dvacc, 32 * w + l32, g32, 1.0f);
   __syncthreads();
-  store_pair_thw<D>(st, dv, g, h, 2 * (int64_t)pair, perm);
+  store_tiles_thw<D>(st, dv, g, h, ta, tb, perm);
   __syncthreads();   // staging area and s_work are reused by the next item
   }
 }
@@ -965,19 +1064,32 @@ hipError_t resident_grid(const void* kernel, unsigned* grid) {
 // Queue order of a sparse launch over the lists (ptr, idx): longest work
 // first inside each XCD's range.  Returns NULL (identity order) for a dense
 // launch or when a range is too long to sort in LDS.
+// With `pairs` (scratch of 3 heads * tiles / 2 ints) the key tiles are also
+// paired by key_pairs_kernel (*pairs_out = the table, cost = union length).
 hipError_t queue_order(const Geometry& g, const int32_t* blk_start, const int32_t* n_blocks, const int32_t* ptr,
                        const int32_t* idx, int32_t* list_tiles, int32_t* order, const int32_t** out,
-                       hipStream_t s) {
+                       int32_t* pairs, const int32_t** pairs_out, hipStream_t s) {
   *out = nullptr;
+  if (pairs_out) *pairs_out = nullptr;
   const int npair = (int)(g.tiles / 2);
   const int total = npair * g.heads;
-  if (ptr == nullptr || order == nullptr || (total + 7) / 8 > kSortMax) return hipSuccess;
+  if (ptr == nullptr || order == nullptr) return hipSuccess;
   hipLaunchKernelGGL(list_tiles_kernel, dim3((unsigned)((g.tiles + 3) / 4), (unsigned)g.heads), dim3(256), 0, s,
                      blk_start, n_blocks, ptr, idx, g.tiles, list_tiles);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(queue_order_kernel, dim3(8), dim3(1024), 0, s, blk_start, n_blocks, list_tiles, g.tiles, npair,
-                     total, order);
+  int32_t* cost = nullptr;
+  if (pairs != nullptr) {
+    cost = pairs + 2 * (int64_t)total;
+    hipLaunchKernelGGL(key_pairs_kernel, dim3((unsigned)(g.tiles / 8), (unsigned)g.heads), dim3(64), 0, s, blk_start,
+                       n_blocks, ptr, idx, list_tiles, g.tiles, pairs, cost);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    *pairs_out = pairs;
+  }
+  if ((total + 7) / 8 > kSortMax) return hipSuccess;
+  hipLaunchKernelGGL(queue_order_kernel, dim3(8), dim3(1024), 0, s, blk_start, n_blocks, list_tiles, cost, g.tiles,
+                     npair, total, order);
   e = hipGetLastError();
   if (e == hipSuccess) *out = order;
   return e;
@@ -993,7 +1105,8 @@ hipError_t fwd_impl(const Geometry& g, float scale, const uint16_t* qp, const ui
   if (e != hipSuccess) return e;
   const int32_t* order = nullptr;
   if (sched != nullptr) {
-    e = queue_order(g, blk_start, n_blocks, row_ptr, col_idx, sched, sched + g.heads * g.tiles, &order, s);
+    e = queue_order(g, blk_start, n_blocks, row_ptr, col_idx, sched, sched + g.heads * g.tiles, &order, nullptr,
+                    nullptr, s);
     if (e != hipSuccess) return e;
   }
   hipLaunchKernelGGL(zero_kernel, dim3(1), dim3(64), 0, s, queues, 8);
@@ -1012,12 +1125,13 @@ hipError_t bwd_impl(const Geometry& g, float scale, const uint16_t* qp, const ui
   hipError_t e = resident_grid((const void*)attn_bwd_dq_kernel<D, DENSE>, &grid_q);
   if (e == hipSuccess) e = resident_grid((const void*)attn_bwd_dkdv_kernel<D, DENSE>, &grid_k);
   if (e != hipSuccess) return e;
-  const int32_t *order_q = nullptr, *order_k = nullptr;
+  const int32_t *order_q = nullptr, *order_k = nullptr, *pairs_k = nullptr;
   if (sched != nullptr) {
     const int64_t lt = (int64_t)g.heads * g.tiles, npairs = (int64_t)g.heads * (g.tiles / 2);
-    e = queue_order(g, blk_start, n_blocks, row_ptr, col_idx, sched, sched + lt, &order_q, s);
+    e = queue_order(g, blk_start, n_blocks, row_ptr, col_idx, sched, sched + lt, &order_q, nullptr, nullptr, s);
     if (e == hipSuccess)
-      e = queue_order(g, blk_start, n_blocks, t_row_ptr, t_col_idx, sched, sched + lt + npairs, &order_k, s);
+      e = queue_order(g, blk_start, n_blocks, t_row_ptr, t_col_idx, sched, sched + lt + npairs, &order_k,
+                      sched + lt + 2 * npairs, &pairs_k, s);
     if (e != hipSuccess) return e;
   }
   hipLaunchKernelGGL(zero_kernel, dim3(1), dim3(64), 0, s, queues, 16);
@@ -1027,7 +1141,7 @@ hipError_t bwd_impl(const Geometry& g, float scale, const uint16_t* qp, const ui
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL((attn_bwd_dkdv_kernel<D, DENSE>), dim3(grid_k), dim3(kThreads), 0, s, g, scale, scale * kLog2e,
                      qp, kp, vp, dop, lse2, delta, perm, blk_start, n_blocks, t_row_ptr, t_col_idx, dk, dv,
-                     queues + 8, order_k);
+                     queues + 8, order_k, pairs_k);
   return hipGetLastError();
 }
 

@@ -47,10 +47,10 @@ hipError_t run_selection(const Geometry& g, const prism_params& p, const int32_t
 // perm) otherwise.  lse may be NULL (not stored).  `queues` is device scratch
 // of kQueueInts ints for the persistent work queues (cleared here, on s);
 // `sched` (NULL: work in index order) is scratch of sched_ints(g, backward)
-// ints for the longest-first queue order.
+// ints for the longest-first queue order (and, backward, the key-tile pairs).
 constexpr int kQueueInts = 64;
 inline int64_t sched_ints(const Geometry& g, bool backward) {
-  return (int64_t)g.heads * g.tiles + (backward ? 2 : 1) * (int64_t)g.heads * (g.tiles / 2);
+  return (int64_t)g.heads * g.tiles + (backward ? 5 : 1) * (int64_t)g.heads * (g.tiles / 2);
 }
 hipError_t launch_attn_fwd(const Geometry& g, float scale, const uint16_t* qp, const uint16_t* kp,
                            const uint16_t* vp, const int32_t* perm, const int32_t* blk_start,
