@@ -8,8 +8,11 @@ Inputs are seeded synthetic tensors already resident in HBM.
 
 Prints one JSON line: fwd+bwd milliseconds per head (the whole layer), the
 achieved MFMA TFLOP/s of the attention kernels, a roofline entry for the
-dominant kernel (HIP-event timed), the in-house dense flash attention on the
-same inputs, and the CPU oracle timed on a bounded sample.
+forward attention kernel (HIP-event timed; its entry point launches it alone
+apart from three small scheduling kernels) and one for the backward entry
+point (bwd_pre, dQ and dK/dV kernels; the dK/dV kernel is the largest of the
+step), the in-house dense flash attention on the same inputs, and the CPU
+oracle timed on a bounded sample.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload 2k]
 """
@@ -341,6 +344,16 @@ def main():
     roof = dict(bound="mfma", kernel="attn_fwd_kernel<128,sparse>", achieved=round(fwd_tflops, 1),
                 peak=PEAK_BF16_TFLOPS, unit="TFLOP/s", frac=round(fwd_tflops / PEAK_BF16_TFLOPS, 4), traffic=traffic,
                 traffic_unit="bytes per launch", flops_per_launch=f_fwd, launch_ms=round(fwd_ms, 4))
+    # the backward entry point: algorithmic F_bwd = 10 D pairs (5 GEMMs); its
+    # kernels execute 14 D pairs (dQ pass: S, dP, dQ; dK/dV pass: S, dP, dV, dK)
+    bwd_ms = stage_ms["attn_bwd"]
+    roof_bwd = dict(bound="mfma", entry_point="prism_attn_bwd",
+                    kernels=["bwd_pre_kernel", "attn_bwd_dq_kernel<128,sparse>", "attn_bwd_dkdv_kernel<128,sparse>"],
+                    achieved=round(bwd_tflops, 1), peak=PEAK_BF16_TFLOPS, unit="TFLOP/s",
+                    frac=round(bwd_tflops / PEAK_BF16_TFLOPS, 4), flops_per_call=f_bwd,
+                    executed_flops_per_call=14 * D * P, executed_frac=round(14 * D * P / (bwd_ms * 1e-3) / 1e12
+                                                                            / PEAK_BF16_TFLOPS, 4),
+                    call_ms=round(bwd_ms, 4))
     line = {
         "metric": "fwd+bwd ms per head at 450K tokens; achieved MFMA TFLOP/s (% of peak)",
         "value": round(ms_step / heads, 3),
@@ -367,6 +380,7 @@ def main():
         "nnz_block_pairs": nnz,
         "token_pairs": pairs,
         "roofline": roof,
+        "roofline_backward": roof_bwd,
         "dense_baseline": dense,
         "speedup_vs_dense": (round(dense["ms_per_head"] / (ms_step / heads), 2) if dense else None),
         "cpu_baseline": cpu,
