@@ -35,19 +35,26 @@ PEAK_HBM_GBS = 8000.0
 # HBM bytes per launch of attn_fwd_kernel at the 2K workload (both heads):
 # FETCH_SIZE x 2.000 + WRITE_SIZE, the factors read from plain 1 GiB copy
 # kernels in the same counter runs.  Valid only for the kernel source the
-# counters were taken on (hash of attn.hip + prism_device.h); reported as
-# null for any other source or workload.
+# counters were taken on (hash of attn.hip + prism_device.h without comments);
+# reported as null for any other source or workload.
 FWD_TRAFFIC = dict(workload="2k", bytes=66_249_967 * 1024,
-                   source_sha256="c5dd32fae3da7217522860ae7eb33e0bd545426dfcb62c8bb4ad6df534776f59")
+                   source_sha256="fb4efe1e1c3dfe2f6a847768e3634769dbce40c202b898f56359afbe02b0cfdc")
 
 
-def attn_source_sha256() -> str:
+def attn_source_sha256(base: str | None = None) -> str:
+    """Hash of the attention kernel source (attn.hip + prism_device.h) with
+    // comments and blank space removed, so that only a change of code makes
+    the stored counter figures stale."""
     import hashlib
+    import re
     h = hashlib.sha256()
-    base = os.path.join(os.path.dirname(os.path.abspath(__file__)), "dynamic_block_sparse_macro_amd", "csrc")
+    if base is None:
+        base = os.path.join(os.path.dirname(os.path.abspath(__file__)), "dynamic_block_sparse_macro_amd", "csrc")
     for f in ("attn.hip", "prism_device.h"):
-        with open(os.path.join(base, f), "rb") as fh:
-            h.update(fh.read())
+        with open(os.path.join(base, f), encoding="utf-8") as fh:
+            text = fh.read()
+        code = "\n".join(" ".join(re.sub(r"//.*", "", line).split()) for line in text.splitlines())
+        h.update(re.sub(r"\n+", "\n", code).encode())
     return h.hexdigest()
 
 

@@ -8,12 +8,13 @@
 //
 // CDNA4 design:
 //  * every block is 1, 2 or 4 tiles of 64 tokens, so one code path serves
-//    64/128/256-token blocks.  A workgroup (4 waves) owns a pair of adjacent
-//    64-token tiles (query tiles in the forward and dQ passes, key tiles in the
-//    dK/dV pass); each wave owns 32 rows.  The two tiles of a pair lie in one
-//    block or in two 64-token blocks of the same zone; the workgroup walks the
-//    union of their block lists and each wave pair computes only the tiles its
-//    own list holds;
+//    64/128/256-token blocks.  A workgroup (4 waves) owns a pair of 64-token
+//    tiles of one zone (query tiles 2p, 2p + 1 in the forward and dQ passes;
+//    key tiles in the dK/dV pass, paired by list overlap in tile_pairs_kernel);
+//    each wave owns 32 rows.  The two tiles of a pair lie in one block or in
+//    two 64-token blocks of the same zone; the workgroup walks the union of
+//    their block lists and each wave pair computes only the tiles its own list
+//    holds;
 //  * v_mfma_f32_32x32x16_bf16 for every product, computed transposed
 //    (S^T = K Q^T, O^T = V^T P^T, ...) so that the accumulator of one product
 //    is, register for register, the B operand of the next;
