@@ -285,25 +285,33 @@ __global__ __launch_bounds__(64) void emit_rows_kernel(const uint32_t* __restric
   }
 }
 
-// Key-major transpose: one wave per 32 key blocks; rows scanned ascending.
-// count pass (fill == false) writes per-column counts, the fill pass writes
-// the row indices.
+constexpr int kTRows = 256;   // rows of the selection bitmap per transpose chunk
+
+// Key-major index from the selection bitmap, in chunks of kTRows query-block
+// rows: one wave per (32-column word, row chunk, head).  Count pass (fill =
+// false): t_cnt[h][c][j] = entries of column j in chunk c.  Fill pass: the
+// rows of column j in chunk c go, ascending, to t_col from
+// t_ptr[h][j] + t_cnt[h][c][j] on (t_cnt then holds offsets within the
+// column, see chunk_scan_kernel).
 __global__ __launch_bounds__(64) void transpose_kernel(const uint32_t* __restrict__ bitmap, int64_t head_bitmap,
                                                        int nbw, const int32_t* __restrict__ n_blocks, bool fill,
-                                                       int32_t* __restrict__ t_len, const int32_t* __restrict__ t_ptr,
+                                                       int32_t* __restrict__ t_cnt, const int32_t* __restrict__ t_ptr,
                                                        int64_t tiles, const int32_t* __restrict__ total,
                                                        int32_t* __restrict__ t_col) {
-  const int h = blockIdx.y, w = blockIdx.x, lane = threadIdx.x;
+  const int h = blockIdx.z, w = blockIdx.x, c = blockIdx.y, lane = threadIdx.x;
   const int nb = n_blocks[h];
-  if (w * 32 >= nb) return;
+  const int i_lo = c * kTRows, i_hi = min(nb, i_lo + kTRows);
+  if (w * 32 >= nb || i_lo >= nb) return;
   const uint32_t* bm = bitmap + h * head_bitmap;
+  const int nchunk = (int)((tiles + kTRows - 1) / kTRows);
+  int32_t* cnt_row = t_cnt + ((int64_t)h * nchunk + c) * tiles;
+  const int j = w * 32 + lane;
   int64_t off = 0;
-  if (fill && lane < 32 && w * 32 + lane < nb)
-    off = head_base(total, h) + t_ptr[(int64_t)h * (tiles + 1) + w * 32 + lane];
+  if (fill && lane < 32 && j < nb) off = head_base(total, h) + t_ptr[(int64_t)h * (tiles + 1) + j] + cnt_row[j];
   int cnt = 0;
-  for (int i0 = 0; i0 < nb; i0 += 64) {
+  for (int i0 = i_lo; i0 < i_hi; i0 += 64) {
     const int i = i0 + lane;
-    const uint32_t word = i < nb ? bm[(int64_t)i * nbw + w] : 0u;
+    const uint32_t word = i < i_hi ? bm[(int64_t)i * nbw + w] : 0u;
     for (int b = 0; b < 32; ++b) {
       const uint64_t m = __ballot((word >> b) & 1u);
       if (fill) {
@@ -315,7 +323,28 @@ __global__ __launch_bounds__(64) void transpose_kernel(const uint32_t* __restric
       }
     }
   }
-  if (!fill && lane < 32 && w * 32 + lane < nb) t_len[(int64_t)h * tiles + w * 32 + lane] = cnt;
+  if (!fill && lane < 32 && j < nb) cnt_row[j] = cnt;
+}
+
+// Per column j: t_cnt[h][c][j] -> exclusive sum over chunks c' < c, and the
+// column's length into t_len[h][j].
+__global__ __launch_bounds__(256) void chunk_scan_kernel(int32_t* __restrict__ t_cnt,
+                                                         const int32_t* __restrict__ n_blocks, int64_t tiles,
+                                                         int32_t* __restrict__ t_len) {
+  const int h = blockIdx.y;
+  const int j = blockIdx.x * blockDim.x + threadIdx.x;
+  const int nb = n_blocks[h];
+  if (j >= nb) return;
+  const int nchunk = (int)((tiles + kTRows - 1) / kTRows);
+  const int used = (nb + kTRows - 1) / kTRows;
+  int32_t* col = t_cnt + (int64_t)h * nchunk * tiles + j;
+  int run = 0;
+  for (int c = 0; c < used; ++c) {
+    const int x = col[(int64_t)c * tiles];
+    col[(int64_t)c * tiles] = run;
+    run += x;
+  }
+  t_len[(int64_t)h * tiles + j] = run;
 }
 
 // Final pointers: local offsets plus the head's base in the shared index array.
@@ -341,6 +370,7 @@ struct SelectWs {
   uint32_t* bitmap;
   int32_t* row_len;
   int32_t* t_len;
+  int32_t* t_cnt;   // [heads][row chunk][column] counts, then offsets within the column
   int32_t* row_local;
   int32_t* t_local;
   int32_t* nnz;
@@ -357,6 +387,7 @@ static SelectWs carve_select(const Geometry& g, char* base, size_t* bytes) {
   w.bitmap = carve<uint32_t>(p, g.heads * nbmax * nbw);
   w.row_len = carve<int32_t>(p, g.heads * nbmax);
   w.t_len = carve<int32_t>(p, g.heads * nbmax);
+  w.t_cnt = carve<int32_t>(p, g.heads * ((nbmax + kTRows - 1) / kTRows) * nbmax);
   w.row_local = carve<int32_t>(p, g.heads * (nbmax + 1));
   w.t_local = carve<int32_t>(p, g.heads * (nbmax + 1));
   w.nnz = carve<int32_t>(p, g.heads);
@@ -449,14 +480,19 @@ hipError_t run_selection(const Geometry& g, const prism_params& p, const int32_t
     hipLaunchKernelGGL(add_base_kernel, gb, dim3(256), 0, s, w.row_local, row_ptr, g.tiles, w.nnz);
     return hipGetLastError();
   }
-  hipLaunchKernelGGL(transpose_kernel, dim3((unsigned)nbw, (unsigned)g.heads), dim3(64), 0, s, w.bitmap, nbmax * nbw,
-                     (int)nbw, n_blocks, false, w.t_len, w.t_local, g.tiles, w.nnz, t_col_idx);
+  const unsigned nchunk = (unsigned)((nbmax + kTRows - 1) / kTRows);
+  const dim3 gt((unsigned)nbw, nchunk, (unsigned)g.heads);
+  hipLaunchKernelGGL(transpose_kernel, gt, dim3(64), 0, s, w.bitmap, nbmax * nbw, (int)nbw, n_blocks, false, w.t_cnt,
+                     w.t_local, g.tiles, w.nnz, t_col_idx);
+  PRISM_TRY(hipGetLastError());
+  hipLaunchKernelGGL(chunk_scan_kernel, dim3((unsigned)((nbmax + 255) / 256), (unsigned)g.heads), dim3(256), 0, s,
+                     w.t_cnt, n_blocks, g.tiles, w.t_len);
   PRISM_TRY(hipGetLastError());
   hipLaunchKernelGGL(scan_kernel, dim3(g.heads), dim3(1024), 0, s, w.t_len, nbmax, n_blocks, g.tiles, w.t_local,
                      w.t_nnz);
   PRISM_TRY(hipGetLastError());
-  hipLaunchKernelGGL(transpose_kernel, dim3((unsigned)nbw, (unsigned)g.heads), dim3(64), 0, s, w.bitmap, nbmax * nbw,
-                     (int)nbw, n_blocks, true, w.t_len, w.t_local, g.tiles, w.t_nnz, t_col_idx);
+  hipLaunchKernelGGL(transpose_kernel, gt, dim3(64), 0, s, w.bitmap, nbmax * nbw, (int)nbw, n_blocks, true, w.t_cnt,
+                     w.t_local, g.tiles, w.t_nnz, t_col_idx);
   PRISM_TRY(hipGetLastError());
   hipLaunchKernelGGL(add_base_kernel, gb, dim3(256), 0, s, w.row_local, row_ptr, g.tiles, w.nnz);
   PRISM_TRY(hipGetLastError());
