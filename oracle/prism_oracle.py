@@ -28,12 +28,13 @@ Readings where the pages are silent (each is listed with its reason in the
 design notes):
   R1  a is a per-token float32 norm map supplied by the caller; absent = 0.
   R2  v-hat_a,d: variance of the slice means of a along d, normalised to sum
-      to 1 over d (1/3 each when all three are 0).  -- parity unpinned
+      to 1 over d (1/3 each when all three are 0).  Pinned by closed forms
+      (a map varying along one axis; a flat map).
   R3  a-bar(m): min-max normalisation of the zone mean of a over all zones
-      (0 everywhere when max == min).                  -- parity unpinned
+      (0 everywhere when max == min).  Pinned by zones of known means.
   R4  epsilon = 1e-6.
   R5  rho(m) = E(m) / max_m' E(m'), E = sum_d sigma^2_v,d, per head (0 when
-      max E == 0).                                     -- parity unpinned
+      max E == 0).  Pinned by closed-form variances and constant zones.
   R6  rho < tau_256 -> 256; else rho < tau_128 -> 128; else 64.
   R7  candidate shapes: edges in {2, 4, 8}, volume in {64, 128, 256}
       (exactly 16 of them), canonical order by volume, then (b_T, b_H, b_W).
@@ -47,8 +48,8 @@ design notes):
       crossing block included; all blocks if it never does; p >= 1 selects
       all blocks.
   R14 density cap (optional): at most floor(cap * N) key tokens per query
-      block; it trims only the Top-p extension, never below Top-k.
-                                                       -- parity unpinned
+      block; it trims only the Top-p extension, never below Top-k.  Pinned by
+      brute force over every prefix of small rows.
   R15 statistics, shapes and the block index are per head; a is shared.
   R16 no causal mask; the log-sum-exp uses the natural log.
   R17 no block is forced into S_i.
@@ -58,8 +59,9 @@ design notes):
       in every zone; Top-k alone keeps min(k, n_b) blocks; Top-p alone keeps
       the (capped) nucleus, at least one block; video-only guidance drops the
       a-bar v-hat term, audio-only guidance drops r; max(rho, a-bar) is an
-      alternative density.  (max(rho, a-bar): parity unpinned; the others
-      reduce to the method's own rule or to closed cases in the pins.)
+      alternative density.  Each is pinned: the k best scores, the brute-force
+      nucleus, the union identity, the silent-audio identity, and a
+      three-zone map whose rho and a-bar are known exactly.
   R22 the A2V norm a_n = |h-hat_n|_2 is taken over the bf16 values of h-hat
       in float64 (squares exact) and rounded once to float32.
 """

@@ -140,3 +140,29 @@ def test_fixed_shape_tiles_every_zone_alike(sid):
             hh, ww = np.divmod(rem, cfg.W)
             for coord, edge in ((t, bt), (hh, bh), (ww, bw)):
                 assert coord.max() - coord.min() == edge - 1 and coord.min() % edge == 0
+
+
+def test_rho_max_closed_form():
+    """max(rho, a-bar) on three zones along W whose densities and couplings
+    are known exactly: V varies along T with amplitudes 1, 1/2, 0 (so
+    E = E0 (1, 1/4, 0) and rho = (1, 1/4, 0)); the zone means of a are
+    1/8, 3/8, 5/8 (a-bar = 0, 1/2, 1, min-max).  rho' takes rho in zone 0
+    and a-bar in zones 1 and 2: (1, 1/2, 1)."""
+    T, H, W, D = 8, 8, 24, 4
+    t, h, w = np.meshgrid(np.arange(T), np.arange(H), np.arange(W), indexing="ij")
+    amp = np.array([1.0, 0.5, 0.0])[w // 8]
+    field = amp * np.cos(np.pi * (t + 0.5) / 8)                   # along T only
+    u = np.array([1.0, -2.0, 0.5, 3.0])
+    v = (field.reshape(-1)[:, None] * u[None, :])[None]           # [1][N][D]
+    a = (np.array([0.125, 0.375, 0.625])[w // 8] + 0.01 * np.cos(np.pi * (h + 0.5) / 8)).reshape(-1)
+    base = O.zone_statistics(v, a, T, H, W, 1e-6)
+    np.testing.assert_allclose(base["rho"][0], [1.0, 0.25, 0.0], atol=1e-15)
+    np.testing.assert_allclose(base["abar"], [0.0, 0.5, 1.0], atol=1e-14)
+    mx = O.zone_statistics(v, a, T, H, W, 1e-6, O.VARIANT_RHO_MAX_AUDIO)
+    np.testing.assert_allclose(mx["rho"][0], [1.0, 0.5, 1.0], atol=1e-14)
+    # the volumes follow the raised density (tau128 = 0.4, tau256 = 0.2):
+    # 64 everywhere, where rho alone gives 64, 128, 256
+    shapes = O.candidate_shapes()
+    vol = lambda rho: [int(np.prod(shapes[s])) for s in O.plan_shapes(mx["g"], rho, 0.4, 0.2)["shape_id"][0]]
+    assert vol(mx["rho"]) == [64, 64, 64]
+    assert vol(base["rho"]) == [64, 128, 256]
