@@ -14,7 +14,7 @@ def pytest_configure(config):
 
 
 def pytest_collection_modifyitems(config, items):
-    # GPU tests run on a GPU machine; skip them cleanly elsewhere unless asked for.
+    # GPU tests need a visible GPU; without one they are skipped.
     try:
         import torch
         has_gpu = torch.cuda.is_available()

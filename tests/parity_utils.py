@@ -51,7 +51,7 @@ def bf16_dev_to_f32(t) -> np.ndarray:
     return t.view(torch.int16).cpu().numpy().view(np.uint16).astype(np.uint32).__lshift__(16).view(np.float32)
 
 
-class GpuRun:
+class LayerOnGpu:
     """One pass of the whole layer on the GPU, with host copies of every output."""
 
     def __init__(self, wl: Workload, params=None, backward: bool | None = None, layer_kw=None):

@@ -20,7 +20,7 @@ import pytest
 import oracle as O
 from workload import CONFIGS, generate
 
-from parity_utils import (FWD_MAX_ABS, FWD_MEAN_ABS, GRAD_REL_L2, LSE_MAX_ABS, GpuRun, check_partition,
+from parity_utils import (FWD_MAX_ABS, FWD_MEAN_ABS, GRAD_REL_L2, LSE_MAX_ABS, LayerOnGpu, check_partition,
                           check_transpose, check_zone_stats, compare_rows, log, oracle_params, reconcile_shapes,
                           rel_l2)
 
@@ -38,7 +38,7 @@ def test_fullsize_parity(name):
     wl = generate(cfg)
     c = wl.cfg
     op = oracle_params(c)
-    run = GpuRun(wl)
+    run = LayerOnGpu(wl)
     gpu = run.host()
     log("gpu layer done; nnz", run.nnz)
 

@@ -14,7 +14,7 @@ import pytest
 import oracle as O
 from workload import CONFIGS, generate
 
-from parity_utils import (FWD_MAX_ABS, FWD_MEAN_ABS, GpuRun, bf16_dev_to_f32, binding_params, fwd_errors, log,
+from parity_utils import (FWD_MAX_ABS, FWD_MEAN_ABS, LayerOnGpu, bf16_dev_to_f32, binding_params, fwd_errors, log,
                           oracle_params, to_dev)
 
 pytestmark = pytest.mark.gpu
@@ -47,7 +47,7 @@ def test_infer_equals_training_forward(name, over):
     wl = generate(name)
     c = wl.cfg
     par = binding_params(c, **over)
-    ref = GpuRun(wl, params=par, backward=False).host()["o"]
+    ref = LayerOnGpu(wl, params=par, backward=False).host()["o"]
     got, inf = _infer(wl, par)
     np.testing.assert_array_equal(got, ref)
     got2, _ = _infer(wl, par, in_place=True)
@@ -80,7 +80,7 @@ def test_infer_fullsize(name):
     wl = generate(CONFIGS[name])
     c = wl.cfg
     par = binding_params(c)
-    run = GpuRun(wl, params=par, backward=False)
+    run = LayerOnGpu(wl, params=par, backward=False)
     ref = run.host()["o"]
     got, inf = _infer(wl, par)
     np.testing.assert_array_equal(got, ref)

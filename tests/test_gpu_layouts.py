@@ -16,7 +16,7 @@ import pytest
 
 from workload import generate
 
-from parity_utils import GpuRun, bf16_dev_to_f32, binding_params, log, to_dev
+from parity_utils import LayerOnGpu, bf16_dev_to_f32, binding_params, log, to_dev
 
 pytestmark = pytest.mark.gpu
 
@@ -81,7 +81,7 @@ def _run_strided(wl, fused: bool):
 @pytest.mark.parametrize("name,fused", [("par_small", False), ("par_small", True), ("par_d64", True)])
 def test_strided_layouts(name, fused):
     wl = generate(name)
-    ref = GpuRun(wl, backward=True).host()
+    ref = LayerOnGpu(wl, backward=True).host()
     got = _run_strided(wl, fused)
     for key in ("o", "dq", "dk", "dv"):
         np.testing.assert_array_equal(got[key], ref[key], err_msg=key)
@@ -98,7 +98,7 @@ def test_capacity_error_writes_no_index():
     from dynamic_block_sparse_macro_amd import binding as B
     wl = generate("par_cap")
     c = wl.cfg
-    full = GpuRun(wl, backward=False)
+    full = LayerOnGpu(wl, backward=False)
     L = full.layer
     want = [int(x) for x in L.nnz]
     # a second select call with room for fewer pairs than selected
@@ -134,7 +134,7 @@ def test_layer_capacity_retry():
     """PrismLayer grows its index on PRISM_ECAPACITY and retries: results equal
     those of a layer that had room from the start."""
     wl = generate("par_small")
-    a = GpuRun(wl, backward=True).host()
-    b = GpuRun(wl, backward=True, layer_kw=dict(col_cap=1)).host()
+    a = LayerOnGpu(wl, backward=True).host()
+    b = LayerOnGpu(wl, backward=True, layer_kw=dict(col_cap=1)).host()
     for key in ("o", "lse", "dq", "dk", "dv"):
         np.testing.assert_array_equal(a[key], b[key], err_msg=key)

@@ -9,7 +9,7 @@ import pytest
 import oracle as O
 from workload import generate
 
-from parity_utils import (FWD_MAX_ABS, FWD_MEAN_ABS, GRAD_REL_L2, LSE_MAX_ABS, GpuRun, check_operands,
+from parity_utils import (FWD_MAX_ABS, FWD_MEAN_ABS, GRAD_REL_L2, LSE_MAX_ABS, LayerOnGpu, check_operands,
                           check_partition, check_transpose, check_zone_stats, compare_rows, fwd_errors, log,
                           oracle_index_to_device, oracle_params, reconcile_shapes, rel_l2)
 
@@ -82,7 +82,7 @@ def _pipeline_parity(wl, over, near_zero=()):
     c = wl.cfg
     op = oracle_params(c, **over)
     log("case", c.name, "N", c.N, "heads", c.heads, "D", c.head_dim, "variant", op.variant, "fixed", op.fixed_shape)
-    run = GpuRun(wl, params=binding_params(c, **over))
+    run = LayerOnGpu(wl, params=binding_params(c, **over))
     gpu = run.host()
     log("gpu done, nnz", run.nnz)
 
@@ -165,8 +165,8 @@ def _pipeline_parity(wl, over, near_zero=()):
 def test_determinism():
     """Two runs give bitwise equal block indices, outputs and gradients."""
     wl = generate("par_cap")
-    a = GpuRun(wl, backward=True).host()
-    b = GpuRun(wl, backward=True).host()
+    a = LayerOnGpu(wl, backward=True).host()
+    b = LayerOnGpu(wl, backward=True).host()
     for key in ("zstats", "g", "rho", "shape_id", "o", "lse", "dq", "dk", "dv"):
         np.testing.assert_array_equal(a[key], b[key], err_msg=key)
     for ia, ib in zip(a["index"], b["index"]):
@@ -208,7 +208,7 @@ def test_top_p_one_is_dense():
     from parity_utils import binding_params, bf16_dev_to_f32
     wl = generate("par_d64")
     c = wl.cfg
-    run = GpuRun(wl, params=binding_params(c, top_p=1.0), backward=True)
+    run = LayerOnGpu(wl, params=binding_params(c, top_p=1.0), backward=True)
     nb = run.layer.n_blocks.cpu().numpy()
     assert run.nnz == [int(x) ** 2 for x in nb]
     dense = DenseAttention(LayerShape(c.T, c.H, c.W, c.heads, c.head_dim), binding_params(c))

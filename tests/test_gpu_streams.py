@@ -8,7 +8,7 @@ import pytest
 
 from workload import generate
 
-from parity_utils import GpuRun, bf16_dev_to_f32, binding_params, log, to_dev
+from parity_utils import LayerOnGpu, bf16_dev_to_f32, binding_params, log, to_dev
 
 pytestmark = pytest.mark.gpu
 
@@ -38,7 +38,7 @@ def _enqueue_layer(wl, stream):
 def test_side_streams_match_default_stream():
     import torch
     wl = generate("par_small")
-    ref = GpuRun(wl, backward=True).host()
+    ref = LayerOnGpu(wl, backward=True).host()
     s1, s2 = torch.cuda.Stream(), torch.cuda.Stream()   # default priority
     runs = [_enqueue_layer(wl, s) for s in (s1, s2)]
     torch.cuda.synchronize()
