@@ -153,8 +153,8 @@ def cpu_baseline(wl, params_o, pairs_per_head, budget_s: float) -> dict:
 def main():
     args = parse()
     if args.gpus != 1:
-        print(json.dumps({"error": "this build runs on one GPU; multi-GPU sharding is described in the design "
-                                   "notes but not implemented", "n_gpus": args.gpus}))
+        print(json.dumps({"error": "the layer runs on one GPU; head sharding over several GPUs is a design "
+                                   "only (no collectives are implemented)", "n_gpus": args.gpus}))
         sys.exit(2)
     import numpy as np
     import torch
