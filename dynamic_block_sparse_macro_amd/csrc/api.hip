@@ -14,7 +14,10 @@ using prism::Geometry;
 
 namespace {
 
-constexpr int64_t kMaxTokens = 65535LL * 64;  // block indices fit 16 bits
+// The selection sorts one row of block scores (up to N / 64 of them, 8-byte
+// keys) in LDS: 16,384 keys fill 128 KB of the 160 KB.  This also keeps block
+// indices within the 16 bits of the sort key.
+constexpr int64_t kMaxTokens = 16384LL * 64;
 
 int check_problem(const prism_problem* pr, Geometry* g) {
   if (!pr) return PRISM_EINVAL;

@@ -58,7 +58,7 @@ enum prism_status {
 
 /* The latent grid and the head layout of the THW tensors. */
 typedef struct prism_problem {
-  int32_t T, H, W;      /* grid; each a positive multiple of 8; N = T*H*W <= 4,194,240 */
+  int32_t T, H, W;      /* grid; each a positive multiple of 8; N = T*H*W <= 1,048,576 (PRISM_EINVAL above) */
   int32_t heads;        /* heads handled by this call, >= 1 */
   int32_t head_dim;     /* D: 64 or 128 */
   int64_t head_stride;  /* elements between heads in THW tensors (>= 0) */

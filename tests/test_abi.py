@@ -57,10 +57,20 @@ def _prob(**kw):
 @pytest.mark.parametrize("kw,code", [
     (dict(T=12), B.PRISM_EGRID), (dict(W=0), B.PRISM_EGRID), (dict(H=-8), B.PRISM_EGRID),
     (dict(head_dim=96), B.PRISM_EDIM), (dict(heads=0), B.PRISM_EINVAL),
+    # the largest grid: N = 1,048,576 tokens (a selection row of up to 16,384
+    # block scores is sorted in LDS); one token row more is refused
+    (dict(T=8, H=8, W=16392, heads=1), B.PRISM_EINVAL),
 ])
 def test_bad_problem(lib, kw, code):
     st = B.prism_zone_stats(_prob(**kw), B.make_params(), 16, None, 16, 16, 16, check=False)
     assert st == code
+
+
+def test_largest_grid_accepted(lib):
+    ws = ctypes.c_size_t(0)
+    st = B.prism_select_blocks(_prob(T=8, H=8, W=16384, heads=1), B.make_params(), *([None] * 11), 0, None, None,
+                               None, None, ws, check=False)
+    assert st == B.PRISM_OK and ws.value > 0
 
 
 def test_bad_strides(lib):
