@@ -1,5 +1,6 @@
 """GPU parity at the full workload sizes, in the launch configuration the
-benchmark times (the whole layer through the C ABI, all heads in one call).
+benchmark times (the whole layer through the C ABI, all heads in one call),
+and at the largest accepted grid (1,048,576 tokens, 16,384 blocks per row).
 
 The oracle cannot run every output at these sizes, so the checks are:
   * zone statistics, shapes, permutation and block starts: everything, exactly
@@ -31,20 +32,31 @@ ATTN_BLOCKS = 10
 MAX_COLUMN = 64
 
 
-@pytest.mark.parametrize("name", ["720p", "1080p", "2k", "long"])
-def test_fullsize_parity(name):
+# (workload, parameter overrides).  max_grid: the largest accepted grid with
+# every zone cut into 64-token blocks, i.e. the most blocks per selection row
+# (16,384, sorted in LDS).
+FULL = [("720p", {}), ("1080p", {}), ("2k", {}), ("long", {}),
+        ("max_grid", dict(variant=O.VARIANT_FIXED_SHAPE, fixed_shape=0))]
+
+
+@pytest.mark.parametrize("name,over", FULL)
+def test_fullsize_parity(name, over):
+    from parity_utils import binding_params
     cfg = CONFIGS[name]
-    log("case", name, cfg.note, "heads", cfg.heads)
+    log("case", name, cfg.note, "heads", cfg.heads, "overrides", over)
     wl = generate(cfg)
     c = wl.cfg
-    op = oracle_params(c)
-    run = LayerOnGpu(wl)
+    op = oracle_params(c, **over)
+    run = LayerOnGpu(wl, params=binding_params(c, **over))
     gpu = run.host()
-    log("gpu layer done; nnz", run.nnz)
+    log("gpu layer done; nnz", run.nnz, "blocks", [int(x["n_blocks"]) for x in gpu["index"]])
 
-    zs = O.zone_statistics(wl.f32("v"), wl.a, c.T, c.H, c.W, op.eps)
+    zs = O.zone_statistics(wl.f32("v"), wl.a, c.T, c.H, c.W, op.eps, op.variant)
     check_zone_stats(gpu, zs)
-    plan = O.plan_shapes(zs["g"], zs["rho"], op.tau128, op.tau256)
+    fixed = None
+    if op.variant & O.VARIANT_FIXED_SHAPE:
+        fixed = np.full(zs["rho"].shape, op.fixed_shape, np.int64)
+    plan = O.plan_shapes(zs["g"], zs["rho"], op.tau128, op.tau256, forced_shape=fixed)
     forced, zone_ties = reconcile_shapes(gpu["shape_id"], zs, plan, op)
     if zone_ties:
         plan = O.plan_shapes(zs["g"], zs["rho"], op.tau128, op.tau256, forced_shape=forced)
