@@ -1136,13 +1136,14 @@ hipError_t bwd_impl(const Geometry& g, float scale, const uint16_t* qp, const ui
     if (e != hipSuccess) return e;
   }
   hipLaunchKernelGGL(zero_kernel, dim3(1), dim3(64), 0, s, queues, 16);
-  hipLaunchKernelGGL((attn_bwd_dq_kernel<D, DENSE>), dim3(grid_q), dim3(kThreads), 0, s, g, scale, scale * kLog2e, qp,
-                     kp, vp, dop, lse2, delta, perm, blk_start, n_blocks, row_ptr, col_idx, dq, queues, order_q);
-  e = hipGetLastError();
-  if (e != hipSuccess) return e;
+  // the key-major pass first: 0.8% faster at 2K than the other order (same box)
   hipLaunchKernelGGL((attn_bwd_dkdv_kernel<D, DENSE>), dim3(grid_k), dim3(kThreads), 0, s, g, scale, scale * kLog2e,
                      qp, kp, vp, dop, lse2, delta, perm, blk_start, n_blocks, t_row_ptr, t_col_idx, dk, dv,
                      queues + 8, order_k, pairs_k);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL((attn_bwd_dq_kernel<D, DENSE>), dim3(grid_q), dim3(kThreads), 0, s, g, scale, scale * kLog2e, qp,
+                     kp, vp, dop, lse2, delta, perm, blk_start, n_blocks, row_ptr, col_idx, dq, queues, order_q);
   return hipGetLastError();
 }
 
