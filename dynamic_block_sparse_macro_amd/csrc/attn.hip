@@ -10,7 +10,7 @@
 //  * every block is 1, 2 or 4 tiles of 64 tokens, so one code path serves
 //    64/128/256-token blocks.  A workgroup (4 waves) owns a pair of 64-token
 //    tiles of one zone (query tiles 2p, 2p + 1 in the forward and dQ passes;
-//    key tiles in the dK/dV pass, paired by list overlap in tile_pairs_kernel);
+//    key tiles in the dK/dV pass, paired by list overlap in key_pairs_kernel);
 //    each wave owns 32 rows.  The two tiles of a pair lie in one block or in
 //    two 64-token blocks of the same zone; the workgroup walks the union of
 //    their block lists and each wave pair computes only the tiles its own list
