@@ -30,10 +30,12 @@
 //    transposed block index (dK, dV): no float atomics, bitwise reproducible;
 //  * persistent workgroups: the grid holds as many workgroups as the chip
 //    keeps resident, and each takes tile pairs from a work queue, first the
-//    queue of its own XCD (one contiguous eighth of the pairs, so neighbouring
-//    query blocks, which share most key blocks, meet in one L2), then the
-//    others.  Rows differ widely in length, so this balances the XCDs and
-//    leaves no slot waiting on the dispatcher.
+//    queue of its own XCD (one contiguous eighth of every head's pairs, so
+//    neighbouring query blocks, which share most key blocks, meet in one L2),
+//    then the others.  Rows differ widely in length, so this balances the
+//    XCDs and leaves no slot waiting on the dispatcher.  Each queue runs head
+//    by head, longest work first inside a head, so the chip works on one
+//    head's K/V (or Q/dO) at a time.
 
 #include <limits.h>
 
@@ -347,7 +349,7 @@ struct WorkQueue {
   }
 };
 
-// ---- queue order: longest work first inside each XCD's range ----
+// ---- queue order: head by head, longest work first, inside each XCD's range ----
 // Cost of a work item (a pair of 64-token tiles): the key (or query) tiles
 // its lists walk, estimated as the longer of the two lists in tiles.
 
@@ -445,16 +447,29 @@ __global__ __launch_bounds__(64) void key_pairs_kernel(const int32_t* __restrict
 
 constexpr int kSortMax = 4096;   // largest XCD range sorted in LDS
 
-// order[pos] for the XCD range of this workgroup: positions sorted by cost
-// descending, ties by position (a bitonic sort of 64-bit keys in LDS).  The
-// cost of a position is pair_cost[pos] when given, else the longer list of
-// its tiles (2 pair, 2 pair + 1).
+// Work item at position s of the head-interleaved sequence: the pairs are cut
+// into eighths, and each eighth lists every head's pairs of that eighth, head
+// by head.  XCD range x then holds eighth x of every head.
+__device__ __forceinline__ int seq_item(int s, int npair, int heads) {
+  auto a = [&](int e) { return (e * npair + 7) / 8; };
+  int e = 0;
+  while (e < 7 && s >= heads * a(e + 1)) ++e;
+  const int c = a(e + 1) - a(e);
+  const int r = s - heads * a(e);
+  return (r / c) * npair + a(e) + r % c;
+}
+
+// order[pos] for the XCD range of this workgroup: head by head, and inside a
+// head by cost descending, ties by position (a bitonic sort of 64-bit keys in
+// LDS).  The cost of an item is pair_cost[item] when given, else the longer
+// list of its tiles (2 pair, 2 pair + 1).
 __global__ __launch_bounds__(1024) void queue_order_kernel(const int32_t* __restrict__ blk_start,
                                                             const int32_t* __restrict__ n_blocks,
                                                             const int32_t* __restrict__ list_tiles,
                                                             const int32_t* __restrict__ pair_cost, int64_t tiles,
                                                             int npair, int total, int32_t* __restrict__ order) {
   __shared__ uint64_t key[kSortMax];
+  const int heads = total / npair;
   const int per = (total + 7) / 8;
   const int lo = blockIdx.x * per;
   const int hi = lo + per < total ? lo + per : total;
@@ -464,12 +479,12 @@ __global__ __launch_bounds__(1024) void queue_order_kernel(const int32_t* __rest
   for (int i = threadIdx.x; i < n2; i += blockDim.x) {
     uint64_t k = ~0ull;   // padding sorts last
     if (i < n) {
-      const int pos = lo + i;
+      const int w = seq_item(lo + i, npair, heads);
+      const int h = w / npair, pair = w % npair;
       uint32_t cost;
       if (pair_cost != nullptr) {
-        cost = (uint32_t)pair_cost[pos];
+        cost = (uint32_t)pair_cost[w];
       } else {
-        const int h = pos / npair, pair = pos % npair;
         const int32_t* bs = blk_start + (int64_t)h * (tiles + 1);
         const int nb = n_blocks[h];
         const int ba = block_of_tile(bs, nb, 2 * pair);
@@ -478,7 +493,7 @@ __global__ __launch_bounds__(1024) void queue_order_kernel(const int32_t* __rest
         const int ca = lt[ba], cb = lt[bb];
         cost = (uint32_t)(ca > cb ? ca : cb);
       }
-      k = ((uint64_t)(0xffffffffu - cost) << 32) | (uint32_t)i;
+      k = ((uint64_t)h << 56) | ((uint64_t)(0xffffffu - (cost < 0xffffffu ? cost : 0xffffffu)) << 32) | (uint32_t)i;
     }
     key[i] = k;
   }
@@ -498,7 +513,7 @@ __global__ __launch_bounds__(1024) void queue_order_kernel(const int32_t* __rest
       }
       __syncthreads();
     }
-  for (int i = threadIdx.x; i < n; i += blockDim.x) order[lo + i] = lo + (int)(uint32_t)key[i];
+  for (int i = threadIdx.x; i < n; i += blockDim.x) order[lo + i] = seq_item(lo + (int)(uint32_t)key[i], npair, heads);
 }
 
 // the workgroup's next work item (uniform), -1 when all queues are empty
@@ -1062,8 +1077,8 @@ hipError_t resident_grid(const void* kernel, unsigned* grid) {
   return hipSuccess;
 }
 
-// Queue order of a sparse launch over the lists (ptr, idx): longest work
-// first inside each XCD's range.  Returns NULL (identity order) for a dense
+// Queue order of a sparse launch over the lists (ptr, idx): head by head and
+// longest work first inside each XCD's range.  Returns NULL (identity order) for a dense
 // launch or when a range is too long to sort in LDS.
 // With `pairs` (scratch of 3 heads * tiles / 2 ints) the key tiles are also
 // paired by key_pairs_kernel (*pairs_out = the table, cost = union length).
