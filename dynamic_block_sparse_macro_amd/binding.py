@@ -85,8 +85,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         "prism_plan_shapes": [pp, pr, _vp, _vp, _vp, _vp, _vp, _vp, _vp],
         "prism_select_blocks": [pp, pr, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, ctypes.c_int64,
                                 _vp, _vp, _vp, _vp, _P(ctypes.c_size_t), _vp],
-        "prism_attn_fwd": [pp, pr] + [_vp] * 11 + [_P(ctypes.c_size_t), _vp],
-        "prism_attn_bwd": [pp, pr] + [_vp] * 17 + [_P(ctypes.c_size_t), _vp],
+        "prism_attn_fwd": [pp, pr] + [_vp] * 12 + [_P(ctypes.c_size_t), _vp],
+        "prism_attn_bwd": [pp, pr] + [_vp] * 18 + [_P(ctypes.c_size_t), _vp],
         "prism_dense_attn_fwd": [pp, pr, _vp, _vp, _vp, _vp, _vp, _vp, _P(ctypes.c_size_t), _vp],
         "prism_dense_attn_bwd": [pp, pr] + [_vp] * 10 + [_P(ctypes.c_size_t), _vp],
         "prism_a2v_norms": [_vp, ctypes.c_int64, ctypes.c_int32, ctypes.c_int64, _vp, _vp],
@@ -158,18 +158,19 @@ def prism_select_blocks(prob, par, q, k, v, perm, blk_start, n_blocks, qp, kp, v
     return _check("prism_select_blocks", st, allow=(PRISM_ECAPACITY,)) if check else st
 
 
-def prism_attn_fwd(prob, par, qp, kp, vp, perm, blk_start, n_blocks, row_ptr, col_idx, o, lse, ws, ws_bytes,
+def prism_attn_fwd(prob, par, qp, kp, vp, perm, blk_start, n_blocks, row_ptr, col_idx, o, o_lo, lse, ws, ws_bytes,
                    stream=None, check=True):
     st = load_library().prism_attn_fwd(ctypes.byref(prob), ctypes.byref(par), _ptr(qp), _ptr(kp), _ptr(vp),
                                        _ptr(perm), _ptr(blk_start), _ptr(n_blocks), _ptr(row_ptr), _ptr(col_idx),
-                                       _ptr(o), _ptr(lse), _ptr(ws), _ref(ws_bytes), _stream(stream))
+                                       _ptr(o), _ptr(o_lo), _ptr(lse), _ptr(ws), _ref(ws_bytes), _stream(stream))
     return _check("prism_attn_fwd", st) if check else st
 
 
-def prism_attn_bwd(prob, par, qp, kp, vp, o, dout, lse, perm, blk_start, n_blocks, row_ptr, col_idx, t_row_ptr,
-                   t_col_idx, dq, dk, dv, ws, ws_bytes, stream=None, check=True):
+def prism_attn_bwd(prob, par, qp, kp, vp, o, o_lo, dout, lse, perm, blk_start, n_blocks, row_ptr, col_idx,
+                   t_row_ptr, t_col_idx, dq, dk, dv, ws, ws_bytes, stream=None, check=True):
     st = load_library().prism_attn_bwd(
-        ctypes.byref(prob), ctypes.byref(par), _ptr(qp), _ptr(kp), _ptr(vp), _ptr(o), _ptr(dout), _ptr(lse),
+        ctypes.byref(prob), ctypes.byref(par), _ptr(qp), _ptr(kp), _ptr(vp), _ptr(o), _ptr(o_lo), _ptr(dout),
+        _ptr(lse),
         _ptr(perm), _ptr(blk_start), _ptr(n_blocks), _ptr(row_ptr), _ptr(col_idx), _ptr(t_row_ptr),
         _ptr(t_col_idx), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(ws), _ref(ws_bytes), _stream(stream))
     return _check("prism_attn_bwd", st) if check else st

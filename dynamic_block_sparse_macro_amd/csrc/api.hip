@@ -231,8 +231,8 @@ int prism_select_blocks(const prism_problem* prob, const prism_params* par, cons
 
 int prism_attn_fwd(const prism_problem* prob, const prism_params* par, const prism_bf16* qp, const prism_bf16* kp,
                    const prism_bf16* vp, const int32_t* perm, const int32_t* blk_start, const int32_t* n_blocks,
-                   const int32_t* row_ptr, const int32_t* col_idx, prism_bf16* o, float* lse, void* ws,
-                   size_t* ws_bytes, prism_stream stream) {
+                   const int32_t* row_ptr, const int32_t* col_idx, prism_bf16* o, prism_bf16* o_lo, float* lse,
+                   void* ws, size_t* ws_bytes, prism_stream stream) {
   Geometry geo;
   CHECK(check_problem(prob, &geo));
   CHECK(check_params(par));
@@ -246,14 +246,15 @@ int prism_attn_fwd(const prism_problem* prob, const prism_params* par, const pri
   if (!qp || !kp || !vp || !perm || !blk_start || !n_blocks || !row_ptr || !col_idx || !o || !lse)
     return PRISM_EINVAL;
   HIPCALL(prism::launch_attn_fwd(geo, attn_scale(*par, geo.D), qp, kp, vp, perm, blk_start, n_blocks, row_ptr,
-                                 col_idx, o, lse, (int*)ws, (int32_t*)((char*)ws + align256(kQueueBytes)),
+                                 col_idx, o, o_lo, lse, (int*)ws, (int32_t*)((char*)ws + align256(kQueueBytes)),
                                  (hipStream_t)stream));
   return PRISM_OK;
 }
 
 int prism_attn_bwd(const prism_problem* prob, const prism_params* par, const prism_bf16* qp, const prism_bf16* kp,
-                   const prism_bf16* vp, const prism_bf16* o, const prism_bf16* dout, const float* lse,
-                   const int32_t* perm, const int32_t* blk_start, const int32_t* n_blocks, const int32_t* row_ptr,
+                   const prism_bf16* vp, const prism_bf16* o, const prism_bf16* o_lo, const prism_bf16* dout,
+                   const float* lse, const int32_t* perm, const int32_t* blk_start, const int32_t* n_blocks,
+                   const int32_t* row_ptr,
                    const int32_t* col_idx, const int32_t* t_row_ptr, const int32_t* t_col_idx, prism_bf16* dq,
                    prism_bf16* dk, prism_bf16* dv, void* ws, size_t* ws_bytes, prism_stream stream) {
   Geometry geo;
@@ -275,7 +276,7 @@ int prism_attn_bwd(const prism_problem* prob, const prism_params* par, const pri
   float* lse2 = (float*)((char*)delta + align256(sizeof(float) * geo.heads * geo.N));
   int* queues = (int*)((char*)ws + bwd_ws(geo));
   int32_t* sched = (int32_t*)((char*)queues + align256(kQueueBytes));
-  HIPCALL(prism::launch_bwd_pre(geo, o, dout, perm, lse, dop, delta, lse2, s));
+  HIPCALL(prism::launch_bwd_pre(geo, o, o_lo, dout, perm, lse, dop, delta, lse2, s));
   HIPCALL(prism::launch_attn_bwd(geo, attn_scale(*par, geo.D), qp, kp, vp, dop, lse2, delta, perm, blk_start,
                                  n_blocks, row_ptr, col_idx, t_row_ptr, t_col_idx, dq, dk, dv, queues, sched, s));
   return PRISM_OK;
@@ -345,7 +346,8 @@ int prism_infer_fwd(const prism_problem* prob, const prism_params* par, const pr
                                  nullptr, nnz.data(), sel, &status, s));
     if (status != PRISM_OK) return status;
     HIPCALL(prism::launch_permute(g, v + off, perm, vp, nullptr, s));
-    HIPCALL(prism::launch_attn_fwd(g, scale, qp, kp, vp, perm, bs, nb, rp, col, o + off, nullptr, queues, sched, s));
+    HIPCALL(prism::launch_attn_fwd(g, scale, qp, kp, vp, perm, bs, nb, rp, col, o + off, nullptr, nullptr, queues,
+                                   sched, s));
   }
   return PRISM_OK;
 }
@@ -373,7 +375,7 @@ int prism_dense_attn_fwd(const prism_problem* prob, const prism_params* par, con
   HIPCALL(prism::launch_permute(geo, v, nullptr, vp, nullptr, s));
   int* queues = (int*)((char*)ws + 3 * operand_bytes(geo));
   HIPCALL(prism::launch_attn_fwd(geo, attn_scale(*par, geo.D), qp, kp, vp, nullptr, nullptr, nullptr, nullptr,
-                                 nullptr, o, lse, queues, nullptr, s));
+                                 nullptr, o, nullptr, lse, queues, nullptr, s));
   return PRISM_OK;
 }
 
@@ -404,7 +406,7 @@ int prism_dense_attn_bwd(const prism_problem* prob, const prism_params* par, con
   HIPCALL(prism::launch_permute(geo, k, nullptr, kp, nullptr, s));
   HIPCALL(prism::launch_permute(geo, v, nullptr, vp, nullptr, s));
   int* queues = (int*)((char*)ws + 3 * ob + bwd_ws(geo));
-  HIPCALL(prism::launch_bwd_pre(geo, o, dout, nullptr, lse, dop, delta, lse2, s));
+  HIPCALL(prism::launch_bwd_pre(geo, o, nullptr, dout, nullptr, lse, dop, delta, lse2, s));
   HIPCALL(prism::launch_attn_bwd(geo, attn_scale(*par, geo.D), qp, kp, vp, dop, lse2, delta, nullptr, nullptr,
                                  nullptr, nullptr, nullptr, nullptr, nullptr, dq, dk, dv, queues, nullptr, s));
   return PRISM_OK;

@@ -181,6 +181,34 @@ __device__ __forceinline__ void acc_to_stage(uint16_t* st, const floatx16* acc, 
     }
 }
 
+// the same rows' low parts: bf16(x - hi) with hi = bf16(x), x = acc * mul,
+// so that hi + lo carries O to about 16 significant bits
+template <int D>
+__device__ __forceinline__ void acc_to_stage_lo(uint16_t* st, const floatx16* acc, int r, int g, float mul) {
+  constexpr int LD = D + 8;
+  auto lo = [](float x) { return x - bf16_to_f32(f32_to_bf16(x)); };
+#pragma unroll
+  for (int u = 0; u < D / 32; ++u)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int d0 = 32 * u + 8 * j + 4 * g;
+      uint2 v;
+      v.x = pack_bf16x2(lo(acc[u][4 * j] * mul), lo(acc[u][4 * j + 1] * mul));
+      v.y = pack_bf16x2(lo(acc[u][4 * j + 2] * mul), lo(acc[u][4 * j + 3] * mul));
+      *(uint2*)(st + r * LD + d0) = v;
+    }
+}
+
+// write 128 staged rows to 128 contiguous rows of D (block order)
+template <int D>
+__device__ __forceinline__ void store_pair_rows(const uint16_t* st, uint16_t* __restrict__ out) {
+  constexpr int CH = D / 8, LD = D + 8;
+  for (int c = threadIdx.x; c < 2 * kTile * CH; c += kThreads) {
+    const int r = c / CH, k = c % CH;
+    *(uint4*)(out + (int64_t)r * D + k * 8) = *(const uint4*)(st + r * LD + k * 8);
+  }
+}
+
 // write 128 staged rows (two tiles) to THW rows through perm
 template <int D>
 __device__ __forceinline__ void store_pair_thw(const uint16_t* st, uint16_t* __restrict__ out, const Geometry& g,
@@ -535,7 +563,8 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(
     Geometry g, float sl2, const uint16_t* __restrict__ qp, const uint16_t* __restrict__ kp,
     const uint16_t* __restrict__ vp, const int32_t* __restrict__ perm, const int32_t* __restrict__ blk_start,
     const int32_t* __restrict__ n_blocks, const int32_t* __restrict__ row_ptr, const int32_t* __restrict__ col_idx,
-    uint16_t* __restrict__ o, float* __restrict__ lse, int* __restrict__ cnt, const int32_t* __restrict__ order) {
+    uint16_t* __restrict__ o, uint16_t* __restrict__ o_lo, float* __restrict__ lse, int* __restrict__ cnt,
+    const int32_t* __restrict__ order) {
   constexpr int TB = TileGeo<D>::BYTES;
   __shared__ __attribute__((aligned(16))) char stage0[TileGeo<D>::STAGE];   // K, V of even steps
   __shared__ __attribute__((aligned(16))) char stage1[TileGeo<D>::STAGE];   // K, V of odd steps
@@ -676,16 +705,25 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(
   acc_to_stage<D>(st, oacc, 32 * w + l32, g32, inv);
   __syncthreads();
   store_pair_thw<D>(st, o, g, h, 2 * (int64_t)pair, perm);
+  if (o_lo != nullptr) {   // the low parts, block order (for the backward's Delta)
+    __syncthreads();
+    acc_to_stage_lo<D>(st, oacc, 32 * w + l32, g32, inv);
+    __syncthreads();
+    store_pair_rows<D>(st, o_lo + (hN + 2 * (int64_t)pair * kTile) * D);
+  }
   __syncthreads();   // staging area and s_work are reused by the next item
   }
 }
 
 // ---------------------------------------------------------------------------
 // backward pre-pass: dO into the operand layout, -delta = -rowsum(dO * O),
-// lse2 = lse * log2(e)
+// lse2 = lse * log2(e).  O is the bf16 output plus, when the forward kept
+// them (o_lo != NULL, block order), its low parts: Delta from the bf16 O
+// alone carries its rounding (2^-9 relative) into every dS.
 // ---------------------------------------------------------------------------
 template <int D>
 __global__ __launch_bounds__(256) void bwd_pre_kernel(Geometry g, const uint16_t* __restrict__ o,
+                                                      const uint16_t* __restrict__ o_lo,
                                                       const uint16_t* __restrict__ dout,
                                                       const int32_t* __restrict__ perm,
                                                       const float* __restrict__ lse, uint16_t* __restrict__ dop,
@@ -701,13 +739,16 @@ __global__ __launch_bounds__(256) void bwd_pre_kernel(Geometry g, const uint16_t
     const int64_t off = (int64_t)h * g.hstride + n * g.tstride + k * 8;
     const uint4 dv = *(const uint4*)(dout + off);
     const uint4 ov = *(const uint4*)(o + off);
+    const uint4 lv = o_lo != nullptr ? *(const uint4*)(o_lo + (p0 + r) * D + k * 8) : make_uint4(0, 0, 0, 0);
     *(uint4*)(rows + (int64_t)r * D + swz_chunk<D>(r, k) * 8) = dv;
-    const uint32_t a4[4] = {dv.x, dv.y, dv.z, dv.w}, b4[4] = {ov.x, ov.y, ov.z, ov.w};
+    const uint32_t a4[4] = {dv.x, dv.y, dv.z, dv.w}, b4[4] = {ov.x, ov.y, ov.z, ov.w}, c4[4] = {lv.x, lv.y, lv.z, lv.w};
     float acc = 0.0f;
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-      acc += bf16_to_f32((uint16_t)(a4[e] & 0xFFFF)) * bf16_to_f32((uint16_t)(b4[e] & 0xFFFF));
-      acc += bf16_to_f32((uint16_t)(a4[e] >> 16)) * bf16_to_f32((uint16_t)(b4[e] >> 16));
+      acc += bf16_to_f32((uint16_t)(a4[e] & 0xFFFF)) *
+             (bf16_to_f32((uint16_t)(b4[e] & 0xFFFF)) + bf16_to_f32((uint16_t)(c4[e] & 0xFFFF)));
+      acc += bf16_to_f32((uint16_t)(a4[e] >> 16)) *
+             (bf16_to_f32((uint16_t)(b4[e] >> 16)) + bf16_to_f32((uint16_t)(c4[e] >> 16)));
     }
 #pragma unroll
     for (int off2 = CH / 2; off2 > 0; off2 >>= 1) acc += __shfl_xor(acc, off2, CH);
@@ -1114,7 +1155,8 @@ hipError_t queue_order(const Geometry& g, const int32_t* blk_start, const int32_
 template <int D, bool DENSE>
 hipError_t fwd_impl(const Geometry& g, float scale, const uint16_t* qp, const uint16_t* kp, const uint16_t* vp,
                     const int32_t* perm, const int32_t* blk_start, const int32_t* n_blocks, const int32_t* row_ptr,
-                    const int32_t* col_idx, uint16_t* o, float* lse, int* queues, int32_t* sched, hipStream_t s) {
+                    const int32_t* col_idx, uint16_t* o, uint16_t* o_lo, float* lse, int* queues, int32_t* sched,
+                    hipStream_t s) {
   const void* k = (const void*)attn_fwd_kernel<D, DENSE>;
   unsigned grid = 0;
   hipError_t e = resident_grid(k, &grid);
@@ -1127,7 +1169,7 @@ hipError_t fwd_impl(const Geometry& g, float scale, const uint16_t* qp, const ui
   }
   hipLaunchKernelGGL(zero_kernel, dim3(1), dim3(64), 0, s, queues, 8);
   hipLaunchKernelGGL((attn_fwd_kernel<D, DENSE>), dim3(grid), dim3(kThreads), 0, s, g, scale * kLog2e, qp, kp, vp,
-                     perm, blk_start, n_blocks, row_ptr, col_idx, o, lse, queues, order);
+                     perm, blk_start, n_blocks, row_ptr, col_idx, o, o_lo, lse, queues, order);
   return hipGetLastError();
 }
 
@@ -1167,22 +1209,23 @@ hipError_t bwd_impl(const Geometry& g, float scale, const uint16_t* qp, const ui
 hipError_t launch_attn_fwd(const Geometry& g, float scale, const uint16_t* qp, const uint16_t* kp,
                            const uint16_t* vp, const int32_t* perm, const int32_t* blk_start,
                            const int32_t* n_blocks, const int32_t* row_ptr, const int32_t* col_idx, uint16_t* o,
-                           float* lse, int* queues, int32_t* sched, hipStream_t s) {
+                           uint16_t* o_lo, float* lse, int* queues, int32_t* sched, hipStream_t s) {
   const bool dense = row_ptr == nullptr;
 #define PRISM_FWD(DD, DN) \
-  fwd_impl<DD, DN>(g, scale, qp, kp, vp, perm, blk_start, n_blocks, row_ptr, col_idx, o, lse, queues, sched, s)
+  fwd_impl<DD, DN>(g, scale, qp, kp, vp, perm, blk_start, n_blocks, row_ptr, col_idx, o, o_lo, lse, queues, sched, s)
   if (g.D == 128) return dense ? PRISM_FWD(128, true) : PRISM_FWD(128, false);
   return dense ? PRISM_FWD(64, true) : PRISM_FWD(64, false);
 #undef PRISM_FWD
 }
 
-hipError_t launch_bwd_pre(const Geometry& g, const uint16_t* o, const uint16_t* dout, const int32_t* perm,
-                          const float* lse, uint16_t* dop, float* delta, float* lse2, hipStream_t s) {
+hipError_t launch_bwd_pre(const Geometry& g, const uint16_t* o, const uint16_t* o_lo, const uint16_t* dout,
+                          const int32_t* perm, const float* lse, uint16_t* dop, float* delta, float* lse2,
+                          hipStream_t s) {
   dim3 grid((unsigned)g.tiles, (unsigned)g.heads);
   if (g.D == 128)
-    hipLaunchKernelGGL(bwd_pre_kernel<128>, grid, dim3(256), 0, s, g, o, dout, perm, lse, dop, delta, lse2);
+    hipLaunchKernelGGL(bwd_pre_kernel<128>, grid, dim3(256), 0, s, g, o, o_lo, dout, perm, lse, dop, delta, lse2);
   else
-    hipLaunchKernelGGL(bwd_pre_kernel<64>, grid, dim3(256), 0, s, g, o, dout, perm, lse, dop, delta, lse2);
+    hipLaunchKernelGGL(bwd_pre_kernel<64>, grid, dim3(256), 0, s, g, o, o_lo, dout, perm, lse, dop, delta, lse2);
   return hipGetLastError();
 }
 

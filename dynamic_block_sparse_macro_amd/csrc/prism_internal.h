@@ -44,7 +44,7 @@ hipError_t run_selection(const Geometry& g, const prism_params& p, const int32_t
 
 // ---- attention (attn.hip) ----
 // Sparse when row_ptr != NULL, dense over all tiles (64-token blocks, identity
-// perm) otherwise.  lse may be NULL (not stored).  `queues` is device scratch
+// perm) otherwise.  lse and o_lo may be NULL (not stored).  `queues` is device scratch
 // of kQueueInts ints for the persistent work queues (cleared here, on s);
 // `sched` (NULL: work in index order) is scratch of sched_ints(g, backward)
 // ints for the longest-first queue order (and, backward, the key-tile pairs).
@@ -55,9 +55,11 @@ inline int64_t sched_ints(const Geometry& g, bool backward) {
 hipError_t launch_attn_fwd(const Geometry& g, float scale, const uint16_t* qp, const uint16_t* kp,
                            const uint16_t* vp, const int32_t* perm, const int32_t* blk_start,
                            const int32_t* n_blocks, const int32_t* row_ptr, const int32_t* col_idx, uint16_t* o,
-                           float* lse, int* queues, int32_t* sched, hipStream_t s);
-hipError_t launch_bwd_pre(const Geometry& g, const uint16_t* o, const uint16_t* dout, const int32_t* perm,
-                          const float* lse, uint16_t* dop, float* delta, float* lse2, hipStream_t s);
+                           uint16_t* o_lo, float* lse, int* queues, int32_t* sched, hipStream_t s);
+// o_lo (NULL: not used): the low bf16 parts of O, [heads][N][D] in block order
+hipError_t launch_bwd_pre(const Geometry& g, const uint16_t* o, const uint16_t* o_lo, const uint16_t* dout,
+                          const int32_t* perm, const float* lse, uint16_t* dop, float* delta, float* lse2,
+                          hipStream_t s);
 hipError_t launch_attn_bwd(const Geometry& g, float scale, const uint16_t* qp, const uint16_t* kp,
                            const uint16_t* vp, const uint16_t* dop, const float* lse2, const float* delta,
                            const int32_t* perm, const int32_t* blk_start, const int32_t* n_blocks,

@@ -74,16 +74,18 @@ class PrismLayer:
         self.col_idx = torch.empty(self.col_cap, dtype=torch.int32, **dev)
         self.t_col_idx = torch.empty_like(self.col_idx)
         self.lse = torch.empty(h, N, dtype=torch.float32, **dev)
+        # low bf16 parts of the forward output (block order), for the backward's rowsum(dO * O)
+        self.o_lo = torch.empty(h, N, D, dtype=torch.bfloat16, **dev)
         self.nnz = (ctypes.c_int64 * h)()
         self.sel_ws_bytes = ctypes.c_size_t(0)
         B.prism_select_blocks(self.prob, params, None, None, None, None, None, None, None, None, None, None, None,
                               0, None, None, None, None, self.sel_ws_bytes)
         self.sel_ws = torch.empty(self.sel_ws_bytes.value, dtype=torch.uint8, **dev)
         self.fwd_ws_bytes = ctypes.c_size_t(0)
-        B.prism_attn_fwd(self.prob, params, *([None] * 11), self.fwd_ws_bytes)
+        B.prism_attn_fwd(self.prob, params, *([None] * 12), self.fwd_ws_bytes)
         self.fwd_ws = torch.empty(self.fwd_ws_bytes.value, dtype=torch.uint8, **dev)
         self.bwd_ws_bytes = ctypes.c_size_t(0)
-        B.prism_attn_bwd(self.prob, params, *([None] * 17), self.bwd_ws_bytes)
+        B.prism_attn_bwd(self.prob, params, *([None] * 18), self.bwd_ws_bytes)
         self.bwd_ws = None
 
     def stream(self):
@@ -114,13 +116,13 @@ class PrismLayer:
 
     def attn_fwd(self, o):
         B.prism_attn_fwd(self.prob, self.params, self.qp, self.kp, self.vp, self.perm, self.blk_start,
-                         self.n_blocks, self.row_ptr, self.col_idx, o, self.lse, self.fwd_ws, self.fwd_ws_bytes,
-                         self.stream())
+                         self.n_blocks, self.row_ptr, self.col_idx, o, self.o_lo, self.lse, self.fwd_ws,
+                         self.fwd_ws_bytes, self.stream())
 
     def attn_bwd(self, o, do, dq, dk, dv):
         if self.bwd_ws is None:
             self.bwd_ws = torch.empty(self.bwd_ws_bytes.value, dtype=torch.uint8, device=self.device)
-        B.prism_attn_bwd(self.prob, self.params, self.qp, self.kp, self.vp, o, do, self.lse, self.perm,
+        B.prism_attn_bwd(self.prob, self.params, self.qp, self.kp, self.vp, o, self.o_lo, do, self.lse, self.perm,
                          self.blk_start, self.n_blocks, self.row_ptr, self.col_idx, self.t_row_ptr, self.t_col_idx,
                          dq, dk, dv, self.bwd_ws, self.bwd_ws_bytes, self.stream())
 
@@ -175,13 +177,13 @@ class PrismInference:
 
 def training_path_bytes(layer: "PrismLayer", nnz_total: int) -> dict:
     """Device bytes of the training path per layer beyond the caller's
-    tensors: what the forward keeps for the backward (permuted operands,
-    LSE, permutation, block starts, both block indices sized to the selected
-    pairs) and the larger of the two transient workspaces (selection,
-    backward), which a caller can share."""
+    tensors: what the forward keeps for the backward (permuted operands, the
+    low parts of O, LSE, permutation, block starts, both block indices sized
+    to the selected pairs) and the larger of the two transient workspaces
+    (selection, backward), which a caller can share."""
     s = layer.shape
     h, N, D, t, Z = s.heads, s.N, s.head_dim, s.tiles, s.Z
-    kept = (3 * h * N * D * 2 + h * N * 4 + h * N * 4 + h * (t + 1) * 4 + h * 4 + 2 * h * (t + 1) * 4
+    kept = (4 * h * N * D * 2 + h * N * 4 + h * N * 4 + h * (t + 1) * 4 + h * 4 + 2 * h * (t + 1) * 4
             + 2 * nnz_total * 4 + h * Z * (8 + 3 + 1) * 8 + h * Z)
     transient = max(layer.sel_ws_bytes.value, layer.bwd_ws_bytes.value, layer.fwd_ws_bytes.value)
     return dict(kept=kept, transient=transient, total=kept + transient)

@@ -179,6 +179,13 @@ int prism_select_blocks(const prism_problem *prob, const prism_params *par, cons
  *
  * qp, kp, vp  operand buffers from prism_select_blocks.
  * o           THW bf16 (out).
+ * o_lo        bf16 [heads][N][D] (out, optional: NULL = not written), block
+ *             order, contiguous: the low part of each output value,
+ *             bf16(O - o) with O the float32 result, so that o + o_lo holds O
+ *             to about 16 significant bits.  prism_attn_bwd takes it to form
+ *             rowsum(dO * O) without the bf16 rounding of o (that rounding,
+ *             2^-9 relative, otherwise reaches every dS and moves dQ by about
+ *             0.6-0.9% relative L2 on the test workloads).
  * lse         float [heads][N] (out), block order: natural-log log-sum-exp
  *             of each query row's scaled scores (kept for the backward).
  * ws, ws_bytes  workspace (the work-queue counters of the persistent
@@ -189,8 +196,8 @@ int prism_select_blocks(const prism_problem *prob, const prism_params *par, cons
  */
 int prism_attn_fwd(const prism_problem *prob, const prism_params *par, const prism_bf16 *qp, const prism_bf16 *kp,
                    const prism_bf16 *vp, const int32_t *perm, const int32_t *blk_start, const int32_t *n_blocks,
-                   const int32_t *row_ptr, const int32_t *col_idx, prism_bf16 *o, float *lse, void *ws,
-                   size_t *ws_bytes, prism_stream stream);
+                   const int32_t *row_ptr, const int32_t *col_idx, prism_bf16 *o, prism_bf16 *o_lo, float *lse,
+                   void *ws, size_t *ws_bytes, prism_stream stream);
 
 /*
  * prism_attn_bwd -- gradients of the sparse attention with respect to Q, K
@@ -198,6 +205,8 @@ int prism_attn_fwd(const prism_problem *prob, const prism_params *par, const pri
  * P_i are constants ([zh/FAQ]).
  *
  * o, dout     THW bf16: forward output and upstream gradient.
+ * o_lo        the low parts of o from prism_attn_fwd, or NULL (rowsum(dO * O)
+ *             is then taken on the bf16 o alone).
  * lse         from prism_attn_fwd.
  * row_ptr/col_idx (query-major) drive dQ; t_row_ptr/t_col_idx (key-major)
  *             drive dK and dV, so no float atomics are used and results are
@@ -206,9 +215,9 @@ int prism_attn_fwd(const prism_problem *prob, const prism_params *par, const pri
  * ws, ws_bytes  workspace (size query as in prism_select_blocks).
  */
 int prism_attn_bwd(const prism_problem *prob, const prism_params *par, const prism_bf16 *qp, const prism_bf16 *kp,
-                   const prism_bf16 *vp, const prism_bf16 *o, const prism_bf16 *dout, const float *lse,
-                   const int32_t *perm, const int32_t *blk_start, const int32_t *n_blocks, const int32_t *row_ptr,
-                   const int32_t *col_idx, const int32_t *t_row_ptr, const int32_t *t_col_idx, prism_bf16 *dq,
+                   const prism_bf16 *vp, const prism_bf16 *o, const prism_bf16 *o_lo, const prism_bf16 *dout,
+                   const float *lse, const int32_t *perm, const int32_t *blk_start, const int32_t *n_blocks,
+                   const int32_t *row_ptr, const int32_t *col_idx, const int32_t *t_row_ptr, const int32_t *t_col_idx, prism_bf16 *dq,
                    prism_bf16 *dk, prism_bf16 *dv, void *ws, size_t *ws_bytes, prism_stream stream);
 
 /*

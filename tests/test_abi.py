@@ -96,8 +96,10 @@ def test_null_pointers(lib):
     assert B.prism_zone_stats(_prob(), B.make_params(), None, None, 16, 16, 16, check=False) == B.PRISM_EINVAL
     assert B.prism_plan_shapes(_prob(), B.make_params(), 16, 16, None, 16, 16, 16, check=False) == B.PRISM_EINVAL
     ok = ctypes.c_size_t(1 << 30)
-    assert B.prism_attn_fwd(_prob(), B.make_params(), *([16] * 9), None, 256, ok, check=False) == B.PRISM_EINVAL
-    assert B.prism_attn_fwd(_prob(), B.make_params(), *([16] * 10), 256, None, check=False) == B.PRISM_EINVAL
+    # lse NULL (o_lo may be NULL)
+    assert B.prism_attn_fwd(_prob(), B.make_params(), *([16] * 9), None, None, 256, ok,
+                            check=False) == B.PRISM_EINVAL
+    assert B.prism_attn_fwd(_prob(), B.make_params(), *([16] * 11), 256, None, check=False) == B.PRISM_EINVAL
 
 
 def test_workspace_queries(lib):
@@ -111,18 +113,18 @@ def test_workspace_queries(lib):
     assert B.prism_select_blocks(prob, par, *([16] * 11), 10, 16, 16, 16, 16, small,
                                  check=False) == B.PRISM_EWORKSPACE
     nb = ctypes.c_size_t(0)
-    assert B.prism_attn_bwd(prob, par, *([None] * 17), nb, check=False) == B.PRISM_OK
+    assert B.prism_attn_bwd(prob, par, *([None] * 18), nb, check=False) == B.PRISM_OK
     assert nb.value >= 2 * 4096 * 128 * 2 + 2 * 4 * 2 * 4096
     nf = ctypes.c_size_t(0)
-    assert B.prism_attn_fwd(prob, par, *([None] * 11), nf, check=False) == B.PRISM_OK
+    assert B.prism_attn_fwd(prob, par, *([None] * 12), nf, check=False) == B.PRISM_OK
     assert nf.value >= 32 + 4 * (4096 // 64) * 2 * 3 // 2   # queue counters, list lengths, queue order
     small_f = ctypes.c_size_t(nf.value - 1)
-    assert B.prism_attn_fwd(prob, par, *([16] * 10), 256, small_f, check=False) == B.PRISM_EWORKSPACE
+    assert B.prism_attn_fwd(prob, par, *([16] * 11), 256, small_f, check=False) == B.PRISM_EWORKSPACE
     nd = ctypes.c_size_t(0)
     assert B.prism_dense_attn_fwd(prob, par, None, None, None, None, None, None, nd, check=False) == B.PRISM_OK
     assert nd.value >= 3 * 2 * 4096 * 128 * 2
     assert B.prism_select_blocks(prob, par, *([16] * 11), -1, 16, 16, 16, 16, n, check=False) == B.PRISM_EINVAL
-    assert B.prism_attn_bwd(prob, par, *([16] * 17), None, check=False) == B.PRISM_EINVAL
+    assert B.prism_attn_bwd(prob, par, *([16] * 18), None, check=False) == B.PRISM_EINVAL
 
 
 def test_a2v_norms_validation(lib):

@@ -53,6 +53,43 @@ def test_variant_parity(name, variant, fixed):
     _pipeline_parity(generate(name), dict(variant=variant, fixed_shape=fixed))
 
 
+# selection at its limits: Top-k alone covering every block (every row dense);
+# one block per row (k = 1 with a Top-p and a cap below any block); Top-p only
+# with a p below any block's probability (n_p = 1)
+EXTREMES = [
+    ("par_small", dict(top_k=1_000_000)),
+    ("par_cap", dict(top_k=1, top_p=1e-9, density_cap=1e-6)),
+    ("par_d64", dict(top_k=1, top_p=1e-9, variant=O.VARIANT_TOPP_ONLY)),
+]
+
+
+@pytest.mark.parametrize("name,over", EXTREMES)
+def test_selection_extremes(name, over):
+    _pipeline_parity(generate(name), over)
+
+
+def test_backward_without_low_parts():
+    """prism_attn_bwd with o_lo = NULL takes rowsum(dO * O) on the bf16 O:
+    dV does not depend on it (bitwise equal), dQ and dK move by the bf16
+    rounding of O (about 1% relative L2 at most on this workload)."""
+    import torch
+    from dynamic_block_sparse_macro_amd import binding as B
+    from parity_utils import bf16_dev_to_f32
+    run = LayerOnGpu(generate("par_small"), backward=True)
+    ref = run.host()
+    L = run.layer
+    dq, dk, dv = (torch.empty_like(run.q) for _ in range(3))
+    B.prism_attn_bwd(L.prob, L.params, L.qp, L.kp, L.vp, run.o, None, run.do, L.lse, L.perm, L.blk_start,
+                     L.n_blocks, L.row_ptr, L.col_idx, L.t_row_ptr, L.t_col_idx, dq, dk, dv, L.bwd_ws,
+                     L.bwd_ws_bytes, L.stream())
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(bf16_dev_to_f32(dv), ref["dv"])
+    for nm, t in (("dq", dq), ("dk", dk)):
+        err = rel_l2(bf16_dev_to_f32(t), ref[nm])
+        log(f"{nm} without the low parts of O: relative L2 to the result with them {err:.3e}")
+        assert 0 < err <= 2e-2, nm
+
+
 def _degenerate(name: str):
     """Workloads whose decisions are all ties: the tie policy end to end.
     flat_v   every value vector is 0.5 and a is 0, so every zone has zero
