@@ -37,8 +37,8 @@ PEAK_HBM_GBS = 8000.0
 # kernels in the same counter runs.  Valid only for the kernel source the
 # counters were taken on (hash of attn.hip + prism_device.h without comments);
 # reported as null for any other source or workload.
-FWD_TRAFFIC = dict(workload="2k", bytes=72_108_834 * 1024,
-                   source_sha256="1495d3e5cdf0436066cb9a93837df99f4f809c088b20824e20f65bc72b7d5daf")
+FWD_TRAFFIC = dict(workload="2k", bytes=70_350_533 * 1024,
+                   source_sha256="d6ff519ff9a88635433568fea463eea99c8a65b330ad1532fe43ef836b21462b")
 
 
 def attn_source_sha256(base: str | None = None) -> str:
