@@ -97,23 +97,44 @@ def _degenerate(name: str):
              of volume 256 are at the same distance from l*;
     equal_qk every query and key is the same vector, so every block score is
              equal, P_i is uniform and Top-k, Top-p and the cap all cut a
-             run of equal scores (order by block index)."""
+             run of equal scores (order by block index);
+    peaked   q and k scaled by 4: peaked block probabilities and softmax
+             rows (outputs near single value vectors), so the forward is
+             held to a bound derived for that case (_peaked_bound)."""
     from dataclasses import replace
+    if name == "peaked":
+        # q and k times 4 (exact in bf16): scores 16 times larger, so each
+        # row's weights concentrate on a few keys and the running maximum of
+        # the online softmax jumps by large steps
+        wl = generate("par_small")
+        x4 = lambda bits: ((bits.astype(np.uint32) << 16).view(np.float32) * 4.0).view(np.uint32) >> 16
+        return replace(wl, q_bits=x4(wl.q_bits).astype(wl.q_bits.dtype),
+                       k_bits=x4(wl.k_bits).astype(wl.k_bits.dtype)), (), _peaked_bound(wl)
     if name == "flat_v":
         wl = generate("par_small")
-        return replace(wl, v_bits=np.full_like(wl.v_bits, 0x3F00), a=np.zeros_like(wl.a)), ("dq", "dk")
+        return replace(wl, v_bits=np.full_like(wl.v_bits, 0x3F00), a=np.zeros_like(wl.a)), ("dq", "dk"), None
     wl = generate("par_cap")
     qk = np.full_like(wl.q_bits, 0x3E80)   # 0.25 in every channel
-    return replace(wl, q_bits=qk, k_bits=qk.copy()), ("dq",)
+    return replace(wl, q_bits=qk, k_bits=qk.copy()), ("dq",), None
 
 
-@pytest.mark.parametrize("name", ["flat_v", "equal_qk"])
+@pytest.mark.parametrize("name", ["flat_v", "equal_qk", "peaked"])
 def test_degenerate_inputs(name):
-    wl, near_zero = _degenerate(name)
-    _pipeline_parity(wl, {}, near_zero)
+    wl, near_zero, fwd_max = _degenerate(name)
+    _pipeline_parity(wl, {}, near_zero, fwd_max)
 
 
-def _pipeline_parity(wl, over, near_zero=()):
+def _peaked_bound(wl):
+    """Forward max-abs bound where a few keys carry each row (outputs near
+    the largest |v|, beyond the regime of the fixed 2e-2 bar): the weights
+    are rounded to bf16 before the PV product and their sum (2^-9 relative
+    each, so at most 2^-8 of the row's largest |v|), and O is rounded to
+    bf16 on output (2^-9 of |O| <= that |v|); plus 1e-3 for float32
+    accumulation."""
+    return 3 * 2.0 ** -9 * float(np.abs(wl.f32("v")).max()) + 1e-3
+
+
+def _pipeline_parity(wl, over, near_zero=(), fwd_max=None):
     import torch
     from parity_utils import binding_params
     c = wl.cfg
@@ -173,7 +194,7 @@ def _pipeline_parity(wl, over, near_zero=()):
         mx, mean = fwd_errors(o2h[h], o_ref)
         lse_err = float(np.abs(lse2[h] - lse).max())
         log(f"head {h}: forward max-abs {mx:.3e} mean-abs {mean:.3e} lse max-abs {lse_err:.3e}")
-        assert mx <= FWD_MAX_ABS and mean <= FWD_MEAN_ABS
+        assert mx <= (FWD_MAX_ABS if fwd_max is None else fwd_max) and mean <= FWD_MEAN_ABS
         assert lse_err <= LSE_MAX_ABS
         if alt_rows == 0:
             # the end-to-end run used the same index: outputs are bitwise equal
