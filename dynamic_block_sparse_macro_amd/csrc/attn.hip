@@ -719,7 +719,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(
 // backward pre-pass: dO into the operand layout, -delta = -rowsum(dO * O),
 // lse2 = lse * log2(e).  O is the bf16 output plus, when the forward kept
 // them (o_lo != NULL, block order), its low parts: Delta from the bf16 O
-// alone carries its rounding (2^-9 relative) into every dS.
+// alone carries its rounding (up to 2^-8 relative) into every dS.
 // ---------------------------------------------------------------------------
 template <int D>
 __global__ __launch_bounds__(256) void bwd_pre_kernel(Geometry g, const uint16_t* __restrict__ o,

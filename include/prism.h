@@ -184,7 +184,7 @@ int prism_select_blocks(const prism_problem *prob, const prism_params *par, cons
  *             bf16(O - o) with O the float32 result, so that o + o_lo holds O
  *             to about 16 significant bits.  prism_attn_bwd takes it to form
  *             rowsum(dO * O) without the bf16 rounding of o (that rounding,
- *             2^-9 relative, otherwise reaches every dS and moves dQ by about
+ *             up to 2^-8 relative, otherwise reaches every dS and moves dQ by about
  *             0.6-0.9% relative L2 on the test workloads).
  * lse         float [heads][N] (out), block order: natural-log log-sum-exp
  *             of each query row's scaled scores (kept for the backward).

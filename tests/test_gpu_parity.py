@@ -127,11 +127,11 @@ def test_degenerate_inputs(name):
 def _peaked_bound(wl):
     """Forward max-abs bound where a few keys carry each row (outputs near
     the largest |v|, beyond the regime of the fixed 2e-2 bar): the weights
-    are rounded to bf16 before the PV product and their sum (2^-9 relative
-    each, so at most 2^-8 of the row's largest |v|), and O is rounded to
-    bf16 on output (2^-9 of |O| <= that |v|); plus 1e-3 for float32
-    accumulation."""
-    return 3 * 2.0 ** -9 * float(np.abs(wl.f32("v")).max()) + 1e-3
+    are rounded to bf16 before the PV product and their sum (bf16 keeps 8
+    significant bits: up to 2^-8 relative each, so at most 2^-7 of the row's
+    largest |v|), and O is rounded to bf16 on output (up to 2^-8 of |O| <=
+    that |v|); plus 1e-3 for float32 accumulation."""
+    return 3 * 2.0 ** -8 * float(np.abs(wl.f32("v")).max()) + 1e-3
 
 
 def _pipeline_parity(wl, over, near_zero=(), fwd_max=None):
@@ -208,7 +208,7 @@ def _pipeline_parity(wl, over, near_zero=(), fwd_max=None):
                 if nm in near_zero:
                     # zero in exact arithmetic (every key, or every value, is
                     # the same vector), so the GPU value is rounding noise: dS
-                    # is rounded to bf16 (2^-9) before the dQ / dK products
+                    # is rounded to bf16 (2^-8) before the dQ / dK products
                     # and Delta is taken on the bf16 O.  Bound: 2^-6 of the
                     # gradient scale, which dV (no cancellation) sets.
                     mx_ref, mx_gpu = float(np.abs(gref).max()), float(np.abs(g).max())
