@@ -15,7 +15,7 @@ from parity_utils import (FWD_MAX_ABS, FWD_MEAN_ABS, GRAD_REL_L2, LSE_MAX_ABS, L
 
 pytestmark = pytest.mark.gpu
 
-CASES = ["tiny", "one_zone", "par_d64", "par_small", "par_cap"]
+CASES = ["tiny", "one_zone", "par_d64", "par_small", "par_cap", "par_heads"]
 
 
 def _oracle_head(wl, plan, h, op):

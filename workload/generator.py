@@ -93,6 +93,9 @@ CONFIGS: dict[str, WorkloadConfig] = {
                               note="6,144 tokens, head_dim 64"),
     "one_zone": WorkloadConfig("one_zone", 8, 8, 8, 1, 128, 14, 0.0, 1, 2.0, 0.1, 1, 0.5,
                                note="a single macro-zone"),
+    "par_heads": WorkloadConfig("par_heads", 8, 24, 40, 5, 128, 15, 0.3, 2, 4.0, 0.05, 4, 0.9,
+                                density_cap=0.3, dispersed_frac=0.3,
+                                note="7,680 tokens, five heads (60 tile pairs each: uneven queue eighths)"),
     # the largest grid the library accepts (1,048,576 tokens); with every zone
     # cut into 64-token blocks it has the most blocks a selection row can hold
     "max_grid": WorkloadConfig("max_grid", 16, 128, 512, 1, 128, 4097, 0.6, 3, 8.0, 0.05, 16, 0.9,
