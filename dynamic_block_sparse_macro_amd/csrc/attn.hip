@@ -33,9 +33,10 @@
 //    queue of its own XCD (one contiguous eighth of every head's pairs, so
 //    neighbouring query blocks, which share most key blocks, meet in one L2),
 //    then the others.  Rows differ widely in length, so this balances the
-//    XCDs and leaves no slot waiting on the dispatcher.  Each queue runs head
-//    by head, longest work first inside a head, so the chip works on one
-//    head's K/V (or Q/dO) at a time.
+//    XCDs and leaves no slot waiting on the dispatcher.  Each queue runs
+//    longest work first; when all heads' K/V (or Q/dO) exceed the last-level
+//    cache it runs head by head, so that the chip works on one head's
+//    operands at a time.
 
 #include <limits.h>
 
@@ -474,6 +475,7 @@ __global__ __launch_bounds__(64) void key_pairs_kernel(const int32_t* __restrict
 }
 
 constexpr int kSortMax = 4096;   // largest XCD range sorted in LDS
+constexpr int64_t kLastLevelCache = 256LL << 20;   // MI355X's memory-side cache, bytes
 
 // Work item at position s of the head-interleaved sequence: the pairs are cut
 // into eighths, and each eighth lists every head's pairs of that eighth, head
@@ -487,15 +489,16 @@ __device__ __forceinline__ int seq_item(int s, int npair, int heads) {
   return (r / c) * npair + a(e) + r % c;
 }
 
-// order[pos] for the XCD range of this workgroup: head by head, and inside a
-// head by cost descending, ties by position (a bitonic sort of 64-bit keys in
-// LDS).  The cost of an item is pair_cost[item] when given, else the longer
+// order[pos] for the XCD range of this workgroup: head by head (by_head) or
+// all heads together, by cost descending inside, ties by position (a bitonic
+// sort of 64-bit keys in LDS).  The cost of an item is pair_cost[item] when given, else the longer
 // list of its tiles (2 pair, 2 pair + 1).
 __global__ __launch_bounds__(1024) void queue_order_kernel(const int32_t* __restrict__ blk_start,
                                                             const int32_t* __restrict__ n_blocks,
                                                             const int32_t* __restrict__ list_tiles,
                                                             const int32_t* __restrict__ pair_cost, int64_t tiles,
-                                                            int npair, int total, int32_t* __restrict__ order) {
+                                                            int npair, int total, bool by_head,
+                                                            int32_t* __restrict__ order) {
   __shared__ uint64_t key[kSortMax];
   const int heads = total / npair;
   const int per = (total + 7) / 8;
@@ -521,7 +524,8 @@ __global__ __launch_bounds__(1024) void queue_order_kernel(const int32_t* __rest
         const int ca = lt[ba], cb = lt[bb];
         cost = (uint32_t)(ca > cb ? ca : cb);
       }
-      k = ((uint64_t)h << 56) | ((uint64_t)(0xffffffu - (cost < 0xffffffu ? cost : 0xffffffu)) << 32) | (uint32_t)i;
+      k = ((uint64_t)(by_head ? h : 0) << 56) | ((uint64_t)(0xffffffu - (cost < 0xffffffu ? cost : 0xffffffu)) << 32) |
+          (uint32_t)i;
     }
     key[i] = k;
   }
@@ -1118,8 +1122,8 @@ hipError_t resident_grid(const void* kernel, unsigned* grid) {
   return hipSuccess;
 }
 
-// Queue order of a sparse launch over the lists (ptr, idx): head by head and
-// longest work first inside each XCD's range.  Returns NULL (identity order) for a dense
+// Queue order of a sparse launch over the lists (ptr, idx): longest work
+// first inside each XCD's range (head by head for large launches).  Returns NULL (identity order) for a dense
 // launch or when a range is too long to sort in LDS.
 // With `pairs` (scratch of 3 heads * tiles / 2 ints) the key tiles are also
 // paired by key_pairs_kernel (*pairs_out = the table, cost = union length).
@@ -1145,8 +1149,12 @@ hipError_t queue_order(const Geometry& g, const int32_t* blk_start, const int32_
     *pairs_out = pairs;
   }
   if ((total + 7) / 8 > kSortMax) return hipSuccess;
+  // head by head only when the operands the passes re-read (K and V, or Q
+  // and dO) of all heads exceed the 256 MB last-level cache: otherwise the
+  // order only lengthens the tail
+  const bool by_head = (int64_t)g.heads * 2 * g.N * g.D * 2 > kLastLevelCache;
   hipLaunchKernelGGL(queue_order_kernel, dim3(8), dim3(1024), 0, s, blk_start, n_blocks, list_tiles, cost, g.tiles,
-                     npair, total, order);
+                     npair, total, by_head, order);
   e = hipGetLastError();
   if (e == hipSuccess) *out = order;
   return e;
