@@ -39,7 +39,8 @@ def _infer(wl, params, in_place=False):
 
 CASES = [("tiny", {}), ("one_zone", {}), ("par_d64", {}), ("par_small", {}), ("par_small", dict(pass_heads=1)),
          ("par_cap", dict(pass_heads=1)), ("par_cap", dict(variant=O.VARIANT_TOPK_ONLY)),
-         ("par_cap", dict(variant=O.VARIANT_TOPP_ONLY, pass_heads=1))]
+         ("par_cap", dict(variant=O.VARIANT_TOPP_ONLY, pass_heads=1)),
+         ("par_heads", dict(pass_heads=2))]   # five heads in passes of 2, 2 and 1
 
 
 @pytest.mark.parametrize("name,over", CASES)
