@@ -424,22 +424,23 @@ __device__ __forceinline__ int list_overlap(const int32_t* __restrict__ bs, cons
   return sum;
 }
 
-// Key-tile pairs of the key-major pass, one wave per 8-tile zone.  A zone of
-// eight one-tile blocks (volume 64) pairs its tiles either as (2i, 2i + 1)
-// or as (i, i + 4), whichever walks fewer union steps: the two tiles of a
-// pair share a work item, so the query tiles in one list but not the other
-// leave half of the workgroup idle.  Other zones keep (2i, 2i + 1), which
-// lie in one block and share its list.  pairs[h][p] = (ta, tb); cost[h][p] =
-// the union's length in tiles.
-__global__ __launch_bounds__(64) void key_pairs_kernel(const int32_t* __restrict__ blk_start,
-                                                       const int32_t* __restrict__ n_blocks,
-                                                       const int32_t* __restrict__ ptr,
-                                                       const int32_t* __restrict__ idx,
-                                                       const int32_t* __restrict__ list_tiles, int64_t tiles,
-                                                       int32_t* __restrict__ pairs, int32_t* __restrict__ cost) {
+// Key-tile pairs of the key-major pass, one workgroup per 8-tile zone, one
+// wave per candidate pair.  A zone of eight one-tile blocks (volume 64)
+// pairs its tiles either as (2i, 2i + 1) or as (i, i + 4), whichever walks
+// fewer union steps: the two tiles of a pair share a work item, so the query
+// tiles in one list but not the other leave half of the workgroup idle.
+// Other zones keep (2i, 2i + 1), which lie in one block and share its list.
+// pairs[h][p] = (ta, tb); cost[h][p] = the union's length in tiles.
+__global__ __launch_bounds__(512) void key_pairs_kernel(const int32_t* __restrict__ blk_start,
+                                                        const int32_t* __restrict__ n_blocks,
+                                                        const int32_t* __restrict__ ptr,
+                                                        const int32_t* __restrict__ idx,
+                                                        const int32_t* __restrict__ list_tiles, int64_t tiles,
+                                                        int32_t* __restrict__ pairs, int32_t* __restrict__ cost) {
+  __shared__ int s_u[8];   // union lengths: pairs (2i, 2i + 1), then (i, i + 4)
   const int h = blockIdx.y;
   const int t0 = blockIdx.x * 8;
-  const int lane = threadIdx.x;
+  const int wv = threadIdx.x >> 6;   // one wave per candidate pair
   const int32_t* bs = blk_start + (int64_t)h * (tiles + 1);
   const int32_t* rp = ptr + (int64_t)h * (tiles + 1);
   const int32_t* lt = list_tiles + (int64_t)h * tiles;
@@ -451,26 +452,19 @@ __global__ __launch_bounds__(64) void key_pairs_kernel(const int32_t* __restrict
     const int bb = single ? b0 + tb : block_of_tile(bs, nb, t0 + tb);
     return ba == bb ? lt[ba] : lt[ba] + lt[bb] - list_overlap(bs, rp, idx, ba, bb);
   };
-  int u[4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) u[i] = uni(2 * i, 2 * i + 1);
-  int stride = 1;
-  if (single) {
-    int u4[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) u4[i] = uni(i, i + 4);
-    if (u4[0] + u4[1] + u4[2] + u4[3] < u[0] + u[1] + u[2] + u[3]) {
-      stride = 4;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) u[i] = u4[i];
-    }
+  if (wv < 4 || single) {
+    const int u = wv < 4 ? uni(2 * wv, 2 * wv + 1) : uni(wv - 4, wv);
+    if ((threadIdx.x & 63) == 0) s_u[wv] = u;
   }
-  if (lane < 4) {
-    const int64_t p = (int64_t)h * (tiles / 2) + t0 / 2 + lane;
-    const int ta = stride == 1 ? 2 * lane : lane;
+  __syncthreads();
+  if (threadIdx.x < 4) {
+    const int i = threadIdx.x;
+    const bool by4 = single && s_u[4] + s_u[5] + s_u[6] + s_u[7] < s_u[0] + s_u[1] + s_u[2] + s_u[3];
+    const int64_t p = (int64_t)h * (tiles / 2) + t0 / 2 + i;
+    const int ta = by4 ? i : 2 * i;
     pairs[2 * p] = t0 + ta;
-    pairs[2 * p + 1] = t0 + ta + stride;
-    cost[p] = lane == 0 ? u[0] : lane == 1 ? u[1] : lane == 2 ? u[2] : u[3];
+    pairs[2 * p + 1] = t0 + ta + (by4 ? 4 : 1);
+    cost[p] = by4 ? s_u[4 + i] : s_u[i];
   }
 }
 
@@ -1142,7 +1136,7 @@ hipError_t queue_order(const Geometry& g, const int32_t* blk_start, const int32_
   int32_t* cost = nullptr;
   if (pairs != nullptr) {
     cost = pairs + 2 * (int64_t)total;
-    hipLaunchKernelGGL(key_pairs_kernel, dim3((unsigned)(g.tiles / 8), (unsigned)g.heads), dim3(64), 0, s, blk_start,
+    hipLaunchKernelGGL(key_pairs_kernel, dim3((unsigned)(g.tiles / 8), (unsigned)g.heads), dim3(512), 0, s, blk_start,
                        n_blocks, ptr, idx, list_tiles, g.tiles, pairs, cost);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
