@@ -37,8 +37,8 @@ PEAK_HBM_GBS = 8000.0
 # kernels in the same counter runs.  Valid only for the kernel source the
 # counters were taken on (hash of attn.hip + prism_device.h without comments);
 # reported as null for any other source or workload.
-FWD_TRAFFIC = dict(workload="2k", bytes=70_077_458 * 1024,
-                   source_sha256="13b1b7e828ac22669255f1e91ff66f1d508d26ed5556377ef6e943da4f09fd04")
+FWD_TRAFFIC = dict(workload="2k", bytes=70_277_718 * 1024,
+                   source_sha256="bed312be8825b1b2374f124fc19b6e3e6985622318ae37ffbfd219733f8be240")
 
 
 def attn_source_sha256(base: str | None = None) -> str:
