@@ -82,7 +82,8 @@ __all__ = [
     "partition", "permute_tokens", "unpermute_tokens",
     "pool_blocks", "block_scores", "block_probabilities", "select_row", "select_blocks",
     "csr_from_rows", "csr_transpose",
-    "sparse_attention_fwd", "sparse_attention_bwd", "dense_attention", "dense_attention_bwd",
+    "sparse_attention_fwd", "sparse_attention_bwd", "sparse_attention_key_block_grad",
+    "dense_attention", "dense_attention_bwd",
     "masked_attention_thw", "token_block_map",
     "Params", "run_pipeline", "row_tie_affected", "row_is_valid_alternative",
     "attention_flops", "selected_pairs",
@@ -598,6 +599,32 @@ def sparse_attention_bwd(qp, kp, vp, op, dop, lse, blk_start, row_ptr, col_idx, 
             dv[ks] += dv_part[off:off + n]
             off += n
     return dq, dk, dv
+
+
+def sparse_attention_key_block_grad(qp, kp, vp, op, dop, lse, blk_start, qrows, j, scale):
+    """dK and dV of the tokens of key block j alone ([zh/FAQ]: with S fixed,
+    gradients reach a key token only from the query blocks whose S_i holds
+    its block).  qrows: those query blocks (the column of j in the key-major
+    index).  op and lse need only be valid on the tokens of qrows.  Per query
+    token p and key token t of j:
+        P_pt = exp(scale q_p . k_t - lse_p),  dS_pt = P_pt (dO_p . v_t - dO_p . o_p),
+        dV_t = sum_p P_pt dO_p,  dK_t = scale sum_p dS_pt q_p.
+    Returns (dk_j, dv_j), each [|B_j|][D], float64."""
+    ks = slice(blk_start[j] * 64, blk_start[j + 1] * 64)
+    k = np.asarray(kp[ks], np.float64)
+    v = np.asarray(vp[ks], np.float64)
+    dk = np.zeros_like(k)
+    dv = np.zeros_like(v)
+    for i in qrows:
+        qs = slice(blk_start[i] * 64, blk_start[i + 1] * 64)
+        q = np.asarray(qp[qs], np.float64)
+        o = np.asarray(op[qs], np.float64)
+        do = np.asarray(dop[qs], np.float64)
+        P = np.exp(scale * (q @ k.T) - np.asarray(lse[qs], np.float64)[:, None])
+        dS = P * (do @ v.T - (do * o).sum(axis=1, keepdims=True))
+        dv += P.T @ do
+        dk += scale * (dS.T @ q)
+    return dk, dv
 
 
 def dense_attention(q, k, v, scale):

@@ -128,3 +128,54 @@ def test_flop_accounting():
     pairs = O.selected_pairs(blk_start, row_ptr, col_idx)
     assert pairs == 64 * 256 + 128 * 64 + 128 * 128 + 256 * 256
     assert O.attention_flops(pairs, 128) == (4 * 128 * pairs, 10 * 128 * pairs)
+
+
+def test_key_block_grad_finite_differences():
+    """dK and dV of one key block, from the query blocks that selected it,
+    against central differences of L = sum(O * dO) with the selection fixed."""
+    rng = np.random.default_rng(11)
+    D = 16
+    blk_start = np.array([0, 1, 3, 4])               # blocks of 64, 128, 64 tokens
+    q, k, v, do = (rng.standard_normal((4 * 64, D)) for _ in range(4))
+    row_ptr = np.array([0, 2, 3, 5])
+    col_idx = np.array([0, 2, 1, 0, 1])              # key block 1 is selected by query blocks 1 and 2
+    scale = 0.3
+
+    def loss(k_, v_):
+        o_, _ = O.sparse_attention_fwd(q, k_, v_, blk_start, row_ptr, col_idx, scale)
+        return (o_ * do).sum()
+
+    o, lse = O.sparse_attention_fwd(q, k, v, blk_start, row_ptr, col_idx, scale)
+    for j, qrows in ((1, [1, 2]), (0, [0, 2]), (2, [0])):
+        dk, dv = O.sparse_attention_key_block_grad(q, k, v, o, do, lse, blk_start, qrows, j, scale)
+        base = blk_start[j] * 64
+        h = 1e-6
+        for g, which in ((dk, 0), (dv, 1)):
+            for _ in range(8):
+                t, c = int(rng.integers(g.shape[0])), int(rng.integers(D))
+                args_p, args_m = [k.copy(), v.copy()], [k.copy(), v.copy()]
+                args_p[which][base + t, c] += h
+                args_m[which][base + t, c] -= h
+                fd = (loss(*args_p) - loss(*args_m)) / (2 * h)
+                assert fd == pytest.approx(g[t, c], rel=1e-6, abs=1e-8)
+
+
+def test_key_block_grad_matches_full_backward():
+    """On the tiny workload's own index, the per-key-block gradients over the
+    key-major columns reassemble the full backward's dK and dV."""
+    w, P, res = _pipeline("tiny")
+    h = res["heads"][0]
+    c = w.cfg
+    scale = 1 / math.sqrt(c.head_dim)
+    perm = h["perm"]
+    qp, kp, vp, dop = (O.permute_tokens(w.f32(x)[0], perm) for x in ("q", "k", "v", "do"))
+    o, lse = O.sparse_attention_fwd(qp, kp, vp, h["blk_start"], h["row_ptr"], h["col_idx"], scale)
+    _, dk_full, dv_full = O.sparse_attention_bwd(qp, kp, vp, o, dop, lse, h["blk_start"], h["row_ptr"],
+                                                 h["col_idx"], scale)
+    tp, tc = O.csr_transpose(h["row_ptr"], h["col_idx"], h["n_blocks"])
+    bs = h["blk_start"]
+    for j in range(h["n_blocks"]):
+        dk, dv = O.sparse_attention_key_block_grad(qp, kp, vp, o, dop, lse, bs, tc[tp[j]:tp[j + 1]], j, scale)
+        ks = slice(bs[j] * 64, bs[j + 1] * 64)
+        np.testing.assert_allclose(dk, dk_full[ks], atol=1e-12)
+        np.testing.assert_allclose(dv, dv_full[ks], atol=1e-12)
