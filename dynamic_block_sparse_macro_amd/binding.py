@@ -23,6 +23,7 @@ PRISM_EPARAM = -4
 PRISM_ECAPACITY = -5
 PRISM_EWORKSPACE = -6
 PRISM_EHIP = -7
+PRISM_EINDEX = -8
 
 VARIANT_FIXED_SHAPE = 1
 VARIANT_TOPK_ONLY = 2
@@ -33,7 +34,7 @@ VARIANT_RHO_MAX_AUDIO = 32
 
 ENTRY_POINTS = ("prism_zone_stats", "prism_plan_shapes", "prism_select_blocks", "prism_attn_fwd",
                 "prism_attn_bwd", "prism_dense_attn_fwd", "prism_dense_attn_bwd", "prism_a2v_norms", "prism_infer_fwd",
-                "prism_strerror")
+                "prism_check_index", "prism_strerror")
 
 
 class PrismError(RuntimeError):
@@ -91,6 +92,7 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         "prism_dense_attn_bwd": [pp, pr] + [_vp] * 10 + [_P(ctypes.c_size_t), _vp],
         "prism_a2v_norms": [_vp, ctypes.c_int64, ctypes.c_int32, ctypes.c_int64, _vp, _vp],
         "prism_infer_fwd": [pp, pr, _vp, _vp, _vp, _vp, _vp, _vp, _P(ctypes.c_size_t), _vp],
+        "prism_check_index": [pp] + [_vp] * 7 + [ctypes.c_int64, _vp],
     }
     for name, args in sig.items():
         f = getattr(lib, name)
@@ -199,3 +201,18 @@ def prism_infer_fwd(prob, par, q, k, v, a, o, ws, ws_bytes, stream=None, check=T
     st = load_library().prism_infer_fwd(ctypes.byref(prob), ctypes.byref(par), _ptr(q), _ptr(k), _ptr(v), _ptr(a),
                                         _ptr(o), _ptr(ws), _ref(ws_bytes), _stream(stream))
     return _check("prism_infer_fwd", st) if check else st
+
+
+def prism_check_index(prob, perm, blk_start, n_blocks, row_ptr, col_idx, t_row_ptr, t_col_idx, n_idx, bad=None,
+                      check=True):
+    """Host arrays (numpy int32, C-contiguous, or None); bad: ctypes int64
+    array of 2 (optional).  Returns the status (raises unless check=False)."""
+    def host(a):
+        if a is None:
+            return None
+        assert a.dtype.str == "<i4" and a.flags["C_CONTIGUOUS"], "int32 C-contiguous host array expected"
+        return a.ctypes.data
+    st = load_library().prism_check_index(ctypes.byref(prob), host(perm), host(blk_start), host(n_blocks),
+                                          host(row_ptr), host(col_idx), host(t_row_ptr), host(t_col_idx),
+                                          int(n_idx), _ptr(bad))
+    return _check("prism_check_index", st) if check else st

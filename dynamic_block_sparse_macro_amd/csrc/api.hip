@@ -159,6 +159,7 @@ const char* prism_strerror(int status) {
     case PRISM_ECAPACITY: return "col_cap is smaller than the number of selected block pairs";
     case PRISM_EWORKSPACE: return "workspace missing or too small";
     case PRISM_EHIP: return "HIP runtime error";
+    case PRISM_EINDEX: return "the block index breaks an invariant (prism_check_index)";
     default: return "unknown status";
   }
 }

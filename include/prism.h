@@ -26,9 +26,16 @@
  * - Block order: the permutation of prism_plan_shapes.  Block-order arrays
  *   are dense: element (head, p, c) at (head * N + p) * head_dim + c.
  * - bf16 values are uint16_t bit patterns of bfloat16.
- * - Every call validates all arguments before it launches anything, and
- *   returns PRISM_OK or a negative status; nothing is written on a
- *   validation error.  NaN or Inf inputs give undefined results.
+ * - Every call validates its arguments (pointers, sizes, strides,
+ *   hyper-parameters) before it launches anything, and returns PRISM_OK or a
+ *   negative status; nothing is written on a validation error.  The
+ *   contents of a block index (perm, blk_start, n_blocks and the block
+ *   lists) are trusted by prism_attn_fwd and prism_attn_bwd, which read them
+ *   on the device: an index written by prism_plan_shapes and
+ *   prism_select_blocks is valid by construction; one from elsewhere is
+ *   checked on a host copy with prism_check_index first (a malformed index
+ *   makes the attention kernels read and write out of bounds).  NaN or Inf
+ *   inputs give undefined results.
  * - The library keeps no state between calls; calls on different streams
  *   with disjoint outputs are independent.
  */
@@ -53,7 +60,8 @@ enum prism_status {
   PRISM_EPARAM = -4,     /* eps <= 0, tau256 > tau128, top_k < 1, top_p or density_cap outside (0, 1], scale < 0, bad variant or pass_heads < 0 */
   PRISM_ECAPACITY = -5,  /* col_cap smaller than the number of selected (query block, key block) pairs */
   PRISM_EWORKSPACE = -6, /* workspace NULL-with-size or too small */
-  PRISM_EHIP = -7        /* a HIP runtime call failed */
+  PRISM_EHIP = -7,       /* a HIP runtime call failed */
+  PRISM_EINDEX = -8      /* prism_check_index: the block index breaks an invariant */
 };
 
 /* The latent grid and the head layout of the THW tensors. */
@@ -277,6 +285,36 @@ int prism_dense_attn_bwd(const prism_problem *prob, const prism_params *par, con
  */
 int prism_a2v_norms(const prism_bf16 *h_hat, int64_t n_tokens, int32_t channels, int64_t token_stride, float *a,
                     prism_stream stream);
+
+/*
+ * prism_check_index -- validate a block index held in HOST memory, before it
+ * is passed to prism_attn_fwd / prism_attn_bwd (which trust the index's
+ * contents).  The rules are those every index of the method satisfies
+ * ([pt/M2]: each 8x8x8 zone is cut into equal blocks of 64, 128 or 256
+ * tokens; [pt/M3]: every query block attends to a non-empty set S_i), in the
+ * layout prism_plan_shapes and prism_select_blocks write:
+ *  - n_blocks[h] in [N/256, N/64];
+ *  - blk_start[h]: starts at 0; every block 1, 2 or 4 tiles of 64 tokens,
+ *    aligned to its size and inside one 8-tile zone; entry n_blocks and
+ *    every later one equal N/64;
+ *  - perm[h] (optional, NULL: not checked): a bijection of [0, N);
+ *  - row_ptr/col_idx: offsets counted over all heads (head h starts where
+ *    head h-1 ends, head 0 at 0), at most n_idx entries, entries past
+ *    n_blocks repeating the head's end; every row non-empty, strictly
+ *    ascending key blocks below n_blocks;
+ *  - t_row_ptr/t_col_idx (optional, both NULL: not checked): the same
+ *    layout (lists may be empty), and exactly the transpose of the
+ *    query-major lists.
+ * bad  HOST int64 [2] (out, optional): head and item of the first violation
+ *      (item: block or row b for blk_start and the query-major lists, token
+ *      position for perm, N/64 + 1 + b for key-major list b; -1 for n_blocks).
+ * All pointers are HOST pointers; the call touches no device.  Returns
+ * PRISM_OK, PRISM_EINDEX at the first violation, PRISM_EGRID or PRISM_EINVAL
+ * for bad arguments.
+ */
+int prism_check_index(const prism_problem *prob, const int32_t *perm, const int32_t *blk_start, const int32_t *n_blocks,
+                      const int32_t *row_ptr, const int32_t *col_idx, const int32_t *t_row_ptr,
+                      const int32_t *t_col_idx, int64_t n_idx, int64_t *bad);
 
 /* Human-readable text of a status code (static storage). */
 const char *prism_strerror(int status);
