@@ -11,7 +11,10 @@ be one of the tied options and the oracle adopts it for the later steps.
 from __future__ import annotations
 
 import math
+import os
 import time
+from concurrent.futures import ProcessPoolExecutor
+from multiprocessing import get_context, shared_memory
 
 import numpy as np
 
@@ -54,7 +57,10 @@ def bf16_dev_to_f32(t) -> np.ndarray:
 class LayerOnGpu:
     """One pass of the whole layer on the GPU, with host copies of every output."""
 
-    def __init__(self, wl: Workload, params=None, backward: bool | None = None, layer_kw=None):
+    def __init__(self, wl: Workload, params=None, backward: bool | None = None, layer_kw=None,
+                 fill_nan: bool = False):
+        """fill_nan: every output buffer (O, its low parts, LSE, dQ, dK, dV)
+        starts as NaN, so an element no work item wrote stays NaN."""
         import torch
         from dynamic_block_sparse_macro_amd.pipeline import LayerShape, PrismLayer
         c = wl.cfg
@@ -64,18 +70,30 @@ class LayerOnGpu:
         self.layer = PrismLayer(self.shape, self.params, **(layer_kw or {}))
         self.q, self.k, self.v = (to_dev(b) for b in (wl.q_bits, wl.k_bits, wl.v_bits))
         self.a = torch.from_numpy(wl.a).cuda()
-        self.o = torch.empty_like(self.q)
+
+        def out_like(t):
+            return torch.full_like(t, float("nan")) if fill_nan else torch.empty_like(t)
+
+        self.o = out_like(self.q)
+        if fill_nan:
+            self.layer.lse.fill_(float("nan"))
+            self.layer.o_lo.fill_(float("nan"))
         self.nnz = self.layer.forward(self.q, self.k, self.v, self.a, self.o)
         backward = c.backward if backward is None else backward
         self.backward = backward and wl.do_bits is not None
         if self.backward:
             self.do = to_dev(wl.do_bits)
-            self.dq, self.dk, self.dv = (torch.empty_like(self.q) for _ in range(3))
+            self.dq, self.dk, self.dv = (out_like(self.q) for _ in range(3))
             self.layer.attn_bwd(self.o, self.do, self.dq, self.dk, self.dv)
         torch.cuda.synchronize()
 
+    def check_index(self):
+        """prism_check_index on a host copy of the index the layer holds."""
+        check_device_index(self.layer)
+
     def host(self):
         L = self.layer
+        self.check_index()
         out = dict(zstats=L.zstats.cpu().numpy(), g=L.g.cpu().numpy(), rho=L.rho.cpu().numpy(),
                    shape_id=L.shape_id.cpu().numpy().astype(np.int64), index=L.index_host(),
                    o=bf16_dev_to_f32(self.o), lse=L.lse.cpu().numpy())
@@ -198,6 +216,34 @@ def fwd_errors(o_gpu: np.ndarray, o_ref: np.ndarray) -> tuple[float, float]:
     return float(d.max()), float(d.mean())
 
 
+def fwd_row_bound(vp: np.ndarray, blk_start: np.ndarray, row_ptr: np.ndarray, col_idx: np.ndarray) -> np.ndarray:
+    """Per-token forward error bound (block order) from bf16 rounding alone:
+    the weights are rounded to bf16 before the PV product and in their sum
+    (bf16 keeps 8 significant bits: up to 2^-8 relative each, so at most
+    2^-7 of the largest |v| among the row's selected keys), and O is rounded
+    to bf16 on output (up to 2^-8 of |O|, itself at most that |v|); plus 1e-3
+    for float32 accumulation: 3 * 2^-8 * max over the row's keys of |v| +
+    1e-3.  It exceeds the fixed 2e-2 bar only where outputs approach the
+    largest values (for |O| >= 8 half a bf16 step, 2^-5, is already above
+    2e-2)."""
+    bound = np.zeros(vp.shape[0])
+    vmax = np.abs(vp).max(axis=1)
+    for i in range(blk_start.size - 1):
+        cols = col_idx[row_ptr[i]:row_ptr[i + 1]]
+        m = max(float(vmax[blk_start[j] * 64:blk_start[j + 1] * 64].max()) for j in cols)
+        bound[blk_start[i] * 64:blk_start[i + 1] * 64] = 3 * 2.0 ** -8 * m + 1e-3
+    return bound
+
+
+def check_fwd_elements(o_gpu: np.ndarray, o_ref: np.ndarray, bound_thw: np.ndarray) -> tuple[int, float]:
+    """Every element within max(2e-2, its row's bf16 rounding bound); returns
+    the number of elements beyond 2e-2 and the largest error / bound."""
+    err = np.abs(o_gpu.astype(np.float64) - o_ref)
+    allowed = np.maximum(FWD_MAX_ABS, bound_thw)[:, None]
+    assert (err <= allowed).all(), f"forward error {err.max():.3e} beyond its row bound"
+    return int((err > FWD_MAX_ABS).sum()), float((err / allowed).max())
+
+
 def rel_l2(x: np.ndarray, ref: np.ndarray) -> float:
     return float(np.linalg.norm(x.astype(np.float64) - ref) / max(np.linalg.norm(ref), 1e-300))
 
@@ -232,3 +278,193 @@ def oracle_index_to_device(layer, idx_per_head: list[dict]):
         layer.t_col_idx = torch.empty_like(layer.col_idx)
     layer.col_idx[:col.size].copy_(torch.from_numpy(col))
     layer.t_col_idx[:tcol.size].copy_(torch.from_numpy(tcol))
+    check_device_index(layer)
+
+
+def check_device_index(layer):
+    """The index a layer's attention calls will read (perm, block starts,
+    both block lists, as held on the device) passes prism_check_index."""
+    from dynamic_block_sparse_macro_amd import binding as B
+    host = lambda t: np.ascontiguousarray(t.cpu().numpy().astype(np.int32))
+    B.prism_check_index(layer.prob, host(layer.perm), host(layer.blk_start), host(layer.n_blocks),
+                        host(layer.row_ptr), host(layer.col_idx), host(layer.t_row_ptr), host(layer.t_col_idx),
+                        layer.col_idx.numel())
+
+
+# ----------------------------------------------------------------------------
+# oracle work spread over worker processes (full-size checks)
+# ----------------------------------------------------------------------------
+# Workers are spawned (fresh interpreters that never touch the GPU); the large
+# arrays reach them through shared memory, and each works on a chunk of
+# query-block rows with the oracle's own functions.
+
+def oracle_workers() -> int:
+    try:
+        n = len(os.sched_getaffinity(0))
+    except AttributeError:  # pragma: no cover
+        n = os.cpu_count() or 1
+    return max(1, min(12, n - 2))
+
+
+class SharedArrays:
+    """numpy arrays copied into shared memory, attachable by name."""
+
+    def __init__(self, **arrays):
+        self.shm, self.spec = [], {}
+        for name, a in arrays.items():
+            a = np.ascontiguousarray(a)
+            m = shared_memory.SharedMemory(create=True, size=max(1, a.nbytes))
+            np.ndarray(a.shape, a.dtype, buffer=m.buf)[...] = a
+            self.shm.append(m)
+            self.spec[name] = (m.name, a.shape, a.dtype.str)
+
+    def close(self):
+        for m in self.shm:
+            m.close()
+            m.unlink()
+        self.shm = []
+
+
+_W: dict = {}
+
+
+def _attach(spec: dict, extra: dict, threads: int = 1):
+    from threadpoolctl import threadpool_limits
+    _W.clear()
+    _W["_limits"] = threadpool_limits(threads)   # BLAS threads of this worker
+    _W["_shm"] = []
+    for name, (sname, shape, dt) in spec.items():
+        m = shared_memory.SharedMemory(name=sname)
+        _W["_shm"].append(m)
+        _W[name] = np.ndarray(shape, np.dtype(dt), buffer=m.buf)
+    _W.update(extra)
+
+
+def _select_chunk(rows):
+    """Oracle selection of some query-block rows: (cols, tie, full row when tied)."""
+    sel = O.select_blocks(_W["qp"], _W["kp"], _W["bs"], _W["params"], _W["N"], rows=rows)
+    out = {}
+    for i, r in sel["rows"].items():
+        out[i] = (r["cols"], bool(r["tie"]), r if r["tie"] else None)
+    return out
+
+
+def _fwd_chunk(rows):
+    """Oracle forward of some query blocks over their whole rows: o and lse of their tokens."""
+    bs = _W["bs"]
+    o, lse = O.sparse_attention_fwd(_W["qp"], _W["kp"], _W["vp"], bs, _W["rp"], _W["ci"], _W["scale"], rows=rows)
+    tok = np.concatenate([np.arange(bs[i] * 64, bs[i + 1] * 64) for i in rows])
+    return tok, o[tok], lse[tok]
+
+
+def _pool(arrays: SharedArrays, extra: dict, workers: int):
+    """A spawned process pool; each worker runs its share of the host's cores
+    as BLAS threads."""
+    try:
+        cores = len(os.sched_getaffinity(0))
+    except AttributeError:  # pragma: no cover
+        cores = os.cpu_count() or 1
+    return ProcessPoolExecutor(workers, mp_context=get_context("spawn"), initializer=_attach,
+                               initargs=(arrays.spec, extra, max(1, cores // workers)))
+
+
+def _progress(results, what: str, total: int):
+    """Yield from results, logging every few finished chunks (long oracle
+    runs keep printing)."""
+    t0 = time.perf_counter()
+    for n, r in enumerate(results, 1):
+        if n == total or n % max(1, total // 6) == 0:
+            log(f"  oracle {what}: {n} of {total} chunks ({time.perf_counter() - t0:.1f} s)")
+        yield r
+
+
+def _chunks(rows, n):
+    rows = np.asarray(rows)
+    return [c for c in np.array_split(rows, max(1, min(len(rows), n))) if c.size]
+
+
+def oracle_select_all(qp, kp, blk_start, params: O.Params, N: int, workers: int | None = None) -> dict:
+    """Oracle selection of every query-block row of one head, in parallel.
+    Returns {row: (cols, tie, row dict when tied)}."""
+    workers = workers or oracle_workers()
+    nb = blk_start.size - 1
+    sh = SharedArrays(qp=qp, kp=kp, bs=blk_start)
+    try:
+        with _pool(sh, dict(params=params, N=N), workers) as ex:
+            out = {}
+            chunks = _chunks(np.arange(nb), 6 * workers)
+            for r in _progress(ex.map(_select_chunk, chunks), "selection", len(chunks)):
+                out.update(r)
+    finally:
+        sh.close()
+    return out
+
+
+def oracle_fwd_rows(qp, kp, vp, blk_start, row_ptr, col_idx, scale, rows, workers: int | None = None):
+    """Oracle forward of the query blocks `rows` (whole rows), in parallel.
+    Returns (o, lse) over all tokens, valid on the tokens of `rows`."""
+    workers = workers or oracle_workers()
+    sh = SharedArrays(qp=qp, kp=kp, vp=vp, bs=blk_start, rp=row_ptr, ci=col_idx)
+    o = np.zeros((qp.shape[0], qp.shape[1]))
+    lse = np.zeros(qp.shape[0])
+    try:
+        with _pool(sh, dict(scale=scale), workers) as ex:
+            chunks = _chunks(sorted(int(i) for i in rows), 3 * workers)
+            for tok, ot, lt in _progress(ex.map(_fwd_chunk, chunks), "forward rows", len(chunks)):
+                o[tok] = ot
+                lse[tok] = lt
+    finally:
+        sh.close()
+    return o, lse
+
+
+def compare_all_rows(gidx: dict, osel: dict) -> dict:
+    """Every query-block row of the GPU index against the oracle's selection:
+    bit-exact outside ties, a valid tied alternative inside."""
+    rp, col = gidx["row_ptr"], gidx["col_idx"]
+    ties, alt = 0, 0
+    for i in range(rp.size - 1):
+        g_cols = col[rp[i]:rp[i + 1]]
+        cols, tie, r = osel[i]
+        if np.array_equal(g_cols, cols):
+            ties += int(tie)
+            continue
+        assert tie, f"row {i}: GPU selected {g_cols.size} blocks, oracle {cols.size}, not a tie"
+        assert O.row_is_valid_alternative(r["s"], g_cols, r), f"row {i}: not a valid tie alternative"
+        ties += 1
+        alt += 1
+    return dict(tie_rows=ties, alternative_rows=alt)
+
+
+def _pipeline_head(h):
+    """The oracle's whole pipeline for head h alone, with that head's shapes
+    given (from the all-head plan): per-head results as in run_pipeline."""
+    W = _W
+    res = O.run_pipeline(W["q"][h:h + 1], W["k"][h:h + 1], W["v"][h:h + 1], W["a"], W["T"], W["H"], W["W"],
+                         W["params"], do=W["do"][h:h + 1], forced_shape=W["shape"][h:h + 1])
+    hr = res["heads"][0]
+    for nm in ("o", "dq", "dk", "dv", "o_p"):
+        hr[nm] = hr[nm].astype(np.float32)
+    return hr
+
+
+def oracle_pipeline_heads(wl: Workload, params: O.Params, workers: int | None = None) -> dict:
+    """O.run_pipeline for every head of a workload, heads spread over worker
+    processes: zone statistics and the plan of all heads here (a and a-bar
+    are shared by the heads), then each head's partition, selection, forward
+    and backward in a worker with its planned shapes."""
+    c = wl.cfg
+    zs = O.zone_statistics(wl.f32("v"), wl.a, c.T, c.H, c.W, params.eps, params.variant)
+    forced = None
+    if params.variant & O.VARIANT_FIXED_SHAPE:
+        forced = np.full(zs["rho"].shape, params.fixed_shape, np.int64)
+    plan = O.plan_shapes(zs["g"], zs["rho"], params.tau128, params.tau256, forced)
+    workers = workers or oracle_workers()
+    sh = SharedArrays(q=wl.f32("q"), k=wl.f32("k"), v=wl.f32("v"), do=wl.f32("do"),
+                      a=wl.a if wl.a is not None else np.zeros(c.N, np.float32), shape=plan["shape_id"])
+    try:
+        with _pool(sh, dict(params=params, T=c.T, H=c.H, W=c.W), workers) as ex:
+            heads = list(_progress(ex.map(_pipeline_head, range(c.heads)), "heads", c.heads))
+    finally:
+        sh.close()
+    return dict(zone=zs, plan=plan, heads=heads)

@@ -96,6 +96,12 @@ CONFIGS: dict[str, WorkloadConfig] = {
     "par_heads": WorkloadConfig("par_heads", 8, 24, 40, 5, 128, 15, 0.3, 2, 4.0, 0.05, 4, 0.9,
                                 density_cap=0.3, dispersed_frac=0.3,
                                 note="7,680 tokens, five heads (60 tile pairs each: uneven queue eighths)"),
+    # many heads of a small grid: all heads' K and V (277 MB) exceed the 256 MB
+    # last-level cache, so the attention work queues run head by head, at a
+    # size the oracle checks in full
+    "many_heads": WorkloadConfig("many_heads", 8, 32, 48, 44, 128, 16, 0.3, 2, 4.0, 0.05, 4, 0.9,
+                                 density_cap=0.1, dispersed_frac=0.25,
+                                 note="12,288 tokens, 44 heads (head-by-head queue order)"),
     # the largest grid the library accepts (1,048,576 tokens); with every zone
     # cut into 64-token blocks it has the most blocks a selection row can hold
     "max_grid": WorkloadConfig("max_grid", 16, 128, 512, 1, 128, 4097, 0.6, 3, 8.0, 0.05, 16, 0.9,
