@@ -34,7 +34,7 @@ VARIANT_RHO_MAX_AUDIO = 32
 
 ENTRY_POINTS = ("prism_zone_stats", "prism_plan_shapes", "prism_select_blocks", "prism_attn_fwd",
                 "prism_attn_bwd", "prism_dense_attn_fwd", "prism_dense_attn_bwd", "prism_a2v_norms", "prism_infer_fwd",
-                "prism_check_index", "prism_strerror")
+                "prism_check_index", "prism_attn_fwd_noalloc", "prism_strerror")
 
 
 class PrismError(RuntimeError):
@@ -93,6 +93,7 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         "prism_a2v_norms": [_vp, ctypes.c_int64, ctypes.c_int32, ctypes.c_int64, _vp, _vp],
         "prism_infer_fwd": [pp, pr, _vp, _vp, _vp, _vp, _vp, _vp, _P(ctypes.c_size_t), _vp],
         "prism_check_index": [pp] + [_vp] * 7 + [ctypes.c_int64, _vp],
+        "prism_attn_fwd_noalloc": [pp, pr] + [_vp] * 12,
     }
     for name, args in sig.items():
         f = getattr(lib, name)
@@ -166,6 +167,14 @@ def prism_attn_fwd(prob, par, qp, kp, vp, perm, blk_start, n_blocks, row_ptr, co
                                        _ptr(perm), _ptr(blk_start), _ptr(n_blocks), _ptr(row_ptr), _ptr(col_idx),
                                        _ptr(o), _ptr(o_lo), _ptr(lse), _ptr(ws), _ref(ws_bytes), _stream(stream))
     return _check("prism_attn_fwd", st) if check else st
+
+
+def prism_attn_fwd_noalloc(prob, par, qp, kp, vp, perm, blk_start, n_blocks, row_ptr, col_idx, o, o_lo, lse,
+                           stream=None, check=True):
+    st = load_library().prism_attn_fwd_noalloc(ctypes.byref(prob), ctypes.byref(par), _ptr(qp), _ptr(kp), _ptr(vp),
+                                               _ptr(perm), _ptr(blk_start), _ptr(n_blocks), _ptr(row_ptr),
+                                               _ptr(col_idx), _ptr(o), _ptr(o_lo), _ptr(lse), _stream(stream))
+    return _check("prism_attn_fwd_noalloc", st) if check else st
 
 
 def prism_attn_bwd(prob, par, qp, kp, vp, o, o_lo, dout, lse, perm, blk_start, n_blocks, row_ptr, col_idx,

@@ -6,6 +6,7 @@
 #include <stdint.h>
 #include <string.h>
 
+#include <mutex>
 #include <vector>
 
 #include "prism_internal.h"
@@ -145,6 +146,34 @@ InferLayout infer_layout(const Geometry& geo, const prism_params& p) {
   return L;
 }
 
+// ---- allocation-free forward (prism_attn_fwd_noalloc) ----
+// Its scratch is this array: one copy per GPU, held until the process ends.
+// Host code must not take the array's name as a device address; the address
+// comes from hipGetSymbolAddress, once per device.
+constexpr size_t kStaticScratchBytes = (size_t)4 << 20;
+static __device__ __align__(256) char scratch[kStaticScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch[kMaxDevices];   // device address of `scratch` per device (NULL: not looked up yet)
+
+// `scratch`'s address on the current device
+hipError_t static_scratch(void** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch[dev] == nullptr) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    g_scratch[dev] = p;
+  }
+  *out = g_scratch[dev];
+  return hipSuccess;
+}
+
 }  // namespace
 
 extern "C" {
@@ -246,6 +275,26 @@ int prism_attn_fwd(const prism_problem* prob, const prism_params* par, const pri
   if (*ws_bytes < need) return PRISM_EWORKSPACE;
   if (!qp || !kp || !vp || !perm || !blk_start || !n_blocks || !row_ptr || !col_idx || !o || !lse)
     return PRISM_EINVAL;
+  HIPCALL(prism::launch_attn_fwd(geo, attn_scale(*par, geo.D), qp, kp, vp, perm, blk_start, n_blocks, row_ptr,
+                                 col_idx, o, o_lo, lse, (int*)ws, (int32_t*)((char*)ws + align256(kQueueBytes)),
+                                 (hipStream_t)stream));
+  return PRISM_OK;
+}
+
+int prism_attn_fwd_noalloc(const prism_problem* prob, const prism_params* par, const prism_bf16* qp,
+                           const prism_bf16* kp, const prism_bf16* vp, const int32_t* perm, const int32_t* blk_start,
+                           const int32_t* n_blocks, const int32_t* row_ptr, const int32_t* col_idx, prism_bf16* o,
+                           prism_bf16* o_lo, float* lse, prism_stream stream) {
+  Geometry geo;
+  CHECK(check_problem(prob, &geo));
+  CHECK(check_params(par));
+  if (!qp || !kp || !vp || !perm || !blk_start || !n_blocks || !row_ptr || !col_idx || !o || !lse)
+    return PRISM_EINVAL;
+  if (align256(kQueueBytes) + sched_bytes(geo, false) > kStaticScratchBytes) return PRISM_EWORKSPACE;
+  void* ws = nullptr;
+  HIPCALL(static_scratch(&ws));
+  // the queue counters are cleared by a kernel inside launch_attn_fwd; the
+  // queue order is written before it is read
   HIPCALL(prism::launch_attn_fwd(geo, attn_scale(*par, geo.D), qp, kp, vp, perm, blk_start, n_blocks, row_ptr,
                                  col_idx, o, o_lo, lse, (int*)ws, (int32_t*)((char*)ws + align256(kQueueBytes)),
                                  (hipStream_t)stream));

@@ -208,6 +208,26 @@ int prism_attn_fwd(const prism_problem *prob, const prism_params *par, const pri
                    void *ws, size_t *ws_bytes, prism_stream stream);
 
 /*
+ * prism_attn_fwd_noalloc -- prism_attn_fwd without a workspace argument, for
+ * callers that cannot allocate device memory around the call (work under
+ * stream capture, tight serving loops, harnesses that forbid allocation).
+ * Its scratch (the work-queue counters and the longest-first queue order:
+ * 256 B plus 6 B per 64-token tile of all heads) is a static 4 MiB device
+ * array of the library, one copy per GPU, held until the process ends.  A
+ * problem needing more (heads * N / 64 above about 699,000) returns
+ * PRISM_EWORKSPACE before anything runs.  Every call on one GPU shares that
+ * GPU's array and the array keeps the last call's contents (the counters are
+ * cleared by a kernel at every call): calls that overlap in time on one GPU
+ * (other streams, other host threads) race, so the caller serialises them.
+ * Other arguments, results and errors as prism_attn_fwd; no allocating
+ * routine is called.
+ */
+int prism_attn_fwd_noalloc(const prism_problem *prob, const prism_params *par, const prism_bf16 *qp,
+                           const prism_bf16 *kp, const prism_bf16 *vp, const int32_t *perm, const int32_t *blk_start,
+                           const int32_t *n_blocks, const int32_t *row_ptr, const int32_t *col_idx, prism_bf16 *o,
+                           prism_bf16 *o_lo, float *lse, prism_stream stream);
+
+/*
  * prism_attn_bwd -- gradients of the sparse attention with respect to Q, K
  * and V, through the selected blocks only; the zone statistics, shapes and
  * P_i are constants ([zh/FAQ]).

@@ -160,3 +160,16 @@ def test_infer_workspace_and_validation(lib):
                              check=False) == B.PRISM_EWORKSPACE
     ok = ctypes.c_size_t(n0.value)
     assert B.prism_infer_fwd(prob, B.make_params(), 16, None, 16, None, 16, 16, ok, check=False) == B.PRISM_EINVAL
+
+
+def test_noalloc_forward_rejects_oversize_before_any_launch(lib):
+    """prism_attn_fwd_noalloc's scratch is a fixed 4 MiB device array: a
+    problem that needs more (here 44 heads of the largest grid) is refused
+    with PRISM_EWORKSPACE before anything runs (no GPU is touched)."""
+    prob = B.make_problem(16, 128, 512, 44, 128)
+    par = B.make_params()
+    dummy = 256
+    st = B.prism_attn_fwd_noalloc(prob, par, *([dummy] * 10), dummy, check=False)
+    assert st == B.PRISM_EWORKSPACE
+    st = B.prism_attn_fwd_noalloc(prob, par, *([None] * 10), None, check=False)
+    assert st == B.PRISM_EINVAL
