@@ -75,6 +75,9 @@ def parse():
     ap.add_argument("--no-infer", action="store_true", help="skip the forward-only inference timing")
     ap.add_argument("--a2v-channels", type=int, default=0,
                     help="channels of the A2V producer timing (default heads * head_dim)")
+    ap.add_argument("--dense-reps", type=int, default=5, help="timed dense-baseline runs (median reported)")
+    ap.add_argument("--no-kernel-times", action="store_true",
+                    help="skip the profiled step that gives per-kernel durations (for runs under rocprofv3)")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="first run one plain 512 MiB device-to-device copy (a known-size kernel for HBM counters)")
     return ap.parse_args()
@@ -129,6 +132,7 @@ def cpu_baseline(wl, params_o, pairs_per_head, budget_s: float) -> dict:
     sizes = np.diff(bs) * 64
     t_attn, pairs_done, done = 0.0, 0, 0
     scale = params_o.score_scale(c.head_dim)
+    per_block = []   # (seconds, token pairs) of each sampled query block
     for i in rows:
         cols = sel["rows"][int(i)]["cols"]
         rp = np.zeros(nb + 1, np.int64)
@@ -136,18 +140,77 @@ def cpu_baseline(wl, params_o, pairs_per_head, budget_s: float) -> dict:
         t0 = time.perf_counter()
         op_, lse = O.sparse_attention_fwd(qp, kp, vp, bs, rp, cols, scale, rows=[int(i)])
         O.sparse_attention_bwd(qp, kp, vp, op_, dop, lse, bs, rp, cols, scale, rows=[int(i)])
-        t_attn += time.perf_counter() - t0
+        dt = time.perf_counter() - t0
+        t_attn += dt
         pairs_done += int(sizes[i] * sizes[cols].sum())
+        per_block.append((dt, int(sizes[i] * sizes[cols].sum())))
         done += 1
         if t_attn + t_plan + t_sel > budget_s:
             break
     t_attn_full = t_attn / max(pairs_done, 1) * pairs_per_head
     ms_per_head = 1e3 * (t_plan + t_pool + t_sel_per_row * nb + t_attn_full)
+    # uncertainty of the scaling: the spread of the sampled blocks' seconds
+    # per token pair (the attention term is nearly all of the estimate)
+    rates = np.array([dt / max(pp, 1) for dt, pp in per_block])
+    rel_se = float(rates.std(ddof=1) / rates.mean() / np.sqrt(rates.size)) if rates.size > 1 else None
     return dict(value=round(ms_per_head, 1), unit="ms/head", cores=threads, host_cpus=cores, kind="oracle",
                 sample=(f"head 0: full zone statistics, shapes and partition; pooled scores and selection of "
                         f"{rows.size} of {nb} query-block rows; float64 forward+backward of {done} query blocks "
                         f"({pairs_done} of {pairs_per_head} token pairs); scaled by rows and pairs"),
-                seconds_measured=round(t_plan + t_pool + t_sel + t_attn, 2))
+                seconds_measured=round(t_plan + t_pool + t_sel + t_attn, 2),
+                attention_share=round(t_attn_full * 1e3 / ms_per_head, 4),
+                extrapolation_rel_stderr=(round(rel_se, 4) if rel_se is not None else None))
+
+
+def kernel_figures(step, stream, cfg, pairs: int, args) -> dict:
+    """Device durations of the step's kernels from one step under
+    torch.profiler (after the timed steps), with the algorithmic HBM bytes of
+    the memory-bound kernels and the MFMA work of the attention kernels."""
+    import torch
+    from torch.profiler import ProfilerActivity, profile
+    torch.cuda.synchronize()
+    with profile(activities=[ProfilerActivity.CUDA]) as prof:
+        step()
+        torch.cuda.synchronize()
+    times: dict[str, list[float]] = {}
+    for e in prof.events():
+        if e.device_type.name != "CUDA":
+            continue
+        name = e.name.replace("prism::(anonymous namespace)::", "").replace("void ", "").split("(")[0]
+        times.setdefault(name, []).append(float(e.device_time_total) * 1e-3)   # ms
+    h, N, D = cfg.heads, cfg.N, cfg.head_dim
+    tiles = N // 64
+    hbm = {   # algorithmic bytes of all the step's launches of the kernel
+        # V once per head and the audio map once
+        "zone_stats_kernel<%d>" % D: h * 2 * N * D + 4 * N,
+        # q, k and v: each read from THW through perm and written as tiles;
+        # the q and k launches also write float64 per-tile channel sums
+        "permute_kernel<%d>" % D: 3 * h * (4 * N * D + 4 * N) + 2 * h * tiles * D * 8,
+        # dO, O and its low parts, perm and LSE read; dOp, -Delta and lse2 written
+        "bwd_pre_kernel<%d>" % D: h * (8 * N * D + 20 * N),
+    }
+    out = {"profiled": "one step under torch.profiler after the timed steps"}
+    for name, b in hbm.items():
+        ts = times.get(name)
+        if not ts:
+            continue
+        ms = sum(ts)
+        out[name] = dict(launches=len(ts), ms=round(ms, 4), bytes=int(b), gbps=round(b / (ms * 1e-3) / 1e9, 1),
+                         frac_hbm=round(b / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4))
+    # executed MFMA work per selected token pair: forward S and PV; dQ pass
+    # S, dP and dQ; dK/dV pass S, dP, dV and dK
+    mfma = {"attn_fwd_kernel<%d, false>" % D: 4, "attn_bwd_dq_kernel<%d, false>" % D: 6,
+            "attn_bwd_dkdv_kernel<%d, false>" % D: 8}
+    for name, executed in mfma.items():
+        ts = times.get(name)
+        if not ts:
+            continue
+        ms = sum(ts)
+        f = executed * D * pairs
+        out[name] = dict(ms=round(ms, 4), executed_flops=f, executed_tflops=round(f / (ms * 1e-3) / 1e12, 1),
+                         executed_frac=round(f / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4))
+    out["all_kernels_ms"] = round(sum(sum(v) for v in times.values()), 4)
+    return out
 
 
 def main():
@@ -251,26 +314,43 @@ def main():
     log(f"step {ms_step:.2f} ms; stages {json.dumps({k: round(v, 3) for k, v in stage_ms.items()})}")
     log(f"density {density:.4f}, attention {attn_tflops:.1f} TFLOP/s (fwd {fwd_tflops:.1f}, bwd {bwd_tflops:.1f})")
 
+    kernels = None
+    if not args.no_kernel_times:
+        kernels = kernel_figures(step, stream, cfg, P, args)
+        log("kernels", json.dumps(kernels))
+
     dense = None
     if not args.no_dense:
         log("dense baseline")
         dn = DenseAttention(shape, par, device=dev)
         od = torch.empty_like(q)
-        dn.forward(q, k, v, od)
-        dn.backward(q, k, v, od, do, dq, dk, dv)
+        for _ in range(3):   # warm-ups
+            dn.forward(q, k, v, od)
+            dn.backward(q, k, v, od, do, dq, dk, dv)
         torch.cuda.synchronize()
-        e = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
-        e[0].record(stream)
-        dn.forward(q, k, v, od)
-        e[1].record(stream)
-        dn.backward(q, k, v, od, do, dq, dk, dv)
-        e[2].record(stream)
-        torch.cuda.synchronize()
-        dfwd, dbwd = e[0].elapsed_time(e[1]), e[1].elapsed_time(e[2])
-        fd = 14 * D * heads * cfg.N ** 2
-        dense = dict(fwd_ms=round(dfwd, 2), bwd_ms=round(dbwd, 2), ms_per_head=round((dfwd + dbwd) / heads, 2),
-                     tflops=round(fd / ((dfwd + dbwd) * 1e-3) / 1e12, 1))
+        dts = []
+        for _ in range(args.dense_reps):
+            e = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+            e[0].record(stream)
+            dn.forward(q, k, v, od)
+            e[1].record(stream)
+            dn.backward(q, k, v, od, do, dq, dk, dv)
+            e[2].record(stream)
+            torch.cuda.synchronize()
+            dts.append((e[0].elapsed_time(e[1]), e[1].elapsed_time(e[2])))
+        dfwd = float(np.median([x[0] for x in dts]))
+        dbwd = float(np.median([x[1] for x in dts]))
+        fdf, fdb = 4 * D * heads * cfg.N ** 2, 10 * D * heads * cfg.N ** 2
+        dense = dict(timing=f"median of {args.dense_reps} after 3 warm-ups", fwd_ms=round(dfwd, 2),
+                     bwd_ms=round(dbwd, 2), ms_per_head=round((dfwd + dbwd) / heads, 2),
+                     tflops=round((fdf + fdb) / ((dfwd + dbwd) * 1e-3) / 1e12, 1),
+                     pct_peak=round(100 * (fdf + fdb) / ((dfwd + dbwd) * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 2),
+                     fwd_pct_peak=round(100 * fdf / (dfwd * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 2),
+                     bwd_pct_peak=round(100 * fdb / (dbwd * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 2),
+                     kernels="the sparse path's attention kernels with every key tile selected")
         log("dense", dense)
+        del dn, od
+        torch.cuda.empty_cache()
 
     # audio-to-video norm producer (upstream of the zone statistics, not part
     # of the timed step): HBM-bound read of h-hat
@@ -280,17 +360,23 @@ def main():
     hh = torch.from_numpy(a2v_output(wl, ch).view(np.int16)).to(dev).view(torch.bfloat16)
     an = torch.empty(cfg.N, dtype=torch.float32, device=dev)
     a2v_norms(hh, an)
-    e = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
-    reps = 20
-    torch.cuda.synchronize()
-    e[0].record(stream)
-    for _ in range(reps):
+    # each repetition after a 512 MiB read (twice the 256 MB last-level cache,
+    # clean lines), so h-hat comes from HBM
+    flush = torch.ones(128 << 20, dtype=torch.int32, device=dev)
+    ts = []
+    for _ in range(10):
+        flush.sum()
+        e = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+        e[0].record(stream)
         a2v_norms(hh, an)
-    e[1].record(stream)
-    torch.cuda.synchronize()
-    a2v_ms = e[0].elapsed_time(e[1]) / reps
+        e[1].record(stream)
+        torch.cuda.synchronize()
+        ts.append(e[0].elapsed_time(e[1]))
+    del flush
+    a2v_ms = float(np.median(ts))
     a2v_bytes = cfg.N * (2 * ch + 4)
     producer = dict(kernel="a2v_norm_kernel", channels=ch, ms=round(a2v_ms, 4), bytes=a2v_bytes,
+                    timing="median of 10, each after reading 512 MiB (twice the last-level cache)",
                     gbps=round(a2v_bytes / (a2v_ms * 1e-3) / 1e9, 1),
                     frac_hbm=round(a2v_bytes / (a2v_ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4))
     log("a2v producer", producer)
@@ -388,6 +474,7 @@ def main():
         "token_pairs": pairs,
         "roofline": roof,
         "roofline_backward": roof_bwd,
+        "kernels": kernels,
         "dense_baseline": dense,
         "speedup_vs_dense": (round(dense["ms_per_head"] / (ms_step / heads), 2) if dense else None),
         "cpu_baseline": cpu,
