@@ -626,10 +626,18 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(
       for (int kk = 0; kk < 2; ++kk)
 #pragma unroll
         for (int i = 0; i < 16; ++i) sacc[kk][i] = 0.0f;
+      // every K row operand of the step is read before the first product, so
+      // the products wait for the LDS once instead of once per pair
+      bf16x8 kr[2][D / 16];
 #pragma unroll
       for (int s = 0; s < D / 16; ++s)
 #pragma unroll
-        for (int kk = 0; kk < 2; ++kk) sacc[kk] = mfma32(lds_row<D>(Kt, off, kk, s), qreg[s], sacc[kk]);
+        for (int kk = 0; kk < 2; ++kk) kr[kk][s] = lds_row<D>(Kt, off, kk, s);
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int s = 0; s < D / 16; ++s)
+#pragma unroll
+        for (int kk = 0; kk < 2; ++kk) sacc[kk] = mfma32(kr[kk][s], qreg[s], sacc[kk]);
       // V^T operands do not depend on P: issue their LDS reads before the softmax
       bf16x8 va[2][2][D / 32];
 #pragma unroll
@@ -801,12 +809,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bwd_dq_kernel(
     }
   }
   const float l2 = lse2[hN + qt * kTile + rloc];
-  floatx16 ndelta;   // -delta of this lane's query row: the dP accumulators start here
-  {
-    const float nd = delta[hN + qt * kTile + rloc];
-#pragma unroll
-    for (int i = 0; i < 16; ++i) ndelta[i] = nd;
-  }
+  const float nd = delta[hN + qt * kTile + rloc];   // -delta of this lane's query row: dP starts here
   floatx16 dqacc[D / 32];
 #pragma unroll
   for (int u = 0; u < D / 32; ++u)
@@ -836,13 +839,29 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bwd_dq_kernel(
       const char* Vt = Kt + TB;
 #pragma unroll
       for (int kk = 0; kk < 2; ++kk) {
-        floatx16 sacc, pacc = ndelta;
+        floatx16 sacc, pacc;
 #pragma unroll
-        for (int i = 0; i < 16; ++i) sacc[i] = 0.0f;
+        for (int i = 0; i < 16; ++i) {
+          sacc[i] = 0.0f;
+          pacc[i] = nd;
+        }
+        // the half's K and V row operands are read before its first product,
+        // so the products wait for the LDS once instead of once per pair
+        constexpr int C = D / 32;   // operands read per chunk
 #pragma unroll
-        for (int s = 0; s < D / 16; ++s) {
-          sacc = mfma32(lds_row<D>(Kt, off, kk, s), qreg[s], sacc);
-          pacc = mfma32(lds_row<D>(Vt, off, kk, s), dreg[s], pacc);   // dP - delta
+        for (int c = 0; c < D / 16; c += C) {
+          bf16x8 kr[C], vr[C];
+#pragma unroll
+          for (int s = 0; s < C; ++s) {
+            kr[s] = lds_row<D>(Kt, off, kk, c + s);
+            vr[s] = lds_row<D>(Vt, off, kk, c + s);
+          }
+          __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+          for (int s = 0; s < C; ++s) {
+            sacc = mfma32(kr[s], qreg[c + s], sacc);
+            pacc = mfma32(vr[s], dreg[c + s], pacc);   // dP - delta
+          }
         }
         bf16x8 ka[2][D / 32];   // K^T operands, read before the dS arithmetic
 #pragma unroll
