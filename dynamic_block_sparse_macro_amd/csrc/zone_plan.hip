@@ -52,12 +52,18 @@ __global__ __launch_bounds__(256) void zone_stats_kernel(Geometry g, const uint1
 #pragma unroll
   for (int tl = 0; tl < TPG; ++tl) {
     const int t = zt * kZone + grp * TPG + tl;
-#pragma unroll 2
+    // the plane's 64 loads are issued before its sums: more bytes in flight
+    // per wave (the kernel is bound by HBM latency x parallelism)
+    uint32_t pl[8][8];
+#pragma unroll
     for (int eta = 0; eta < 8; ++eta) {
       const int64_t row = ((int64_t)t * g.H + zh * kZone + eta) * g.W + zw * kZone;
-      uint32_t pr[8];
 #pragma unroll
-      for (int om = 0; om < 8; ++om) pr[om] = *(const uint32_t*)(vb + (row + om) * g.tstride);
+      for (int om = 0; om < 8; ++om) pl[eta][om] = *(const uint32_t*)(vb + (row + om) * g.tstride);
+    }
+#pragma unroll
+    for (int eta = 0; eta < 8; ++eta) {
+      const uint32_t* pr = pl[eta];
 #pragma unroll
       for (int om = 0; om < 8; ++om) {
         const double x0 = (double)bf16_to_f32((uint16_t)(pr[om] & 0xFFFFu));
