@@ -845,23 +845,10 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bwd_dq_kernel(
           sacc[i] = 0.0f;
           pacc[i] = nd;
         }
-        // the half's K and V row operands are read before its first product,
-        // so the products wait for the LDS once instead of once per pair
-        constexpr int C = D / 32;   // operands read per chunk
 #pragma unroll
-        for (int c = 0; c < D / 16; c += C) {
-          bf16x8 kr[C], vr[C];
-#pragma unroll
-          for (int s = 0; s < C; ++s) {
-            kr[s] = lds_row<D>(Kt, off, kk, c + s);
-            vr[s] = lds_row<D>(Vt, off, kk, c + s);
-          }
-          __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-          for (int s = 0; s < C; ++s) {
-            sacc = mfma32(kr[s], qreg[c + s], sacc);
-            pacc = mfma32(vr[s], dreg[c + s], pacc);   // dP - delta
-          }
+        for (int s = 0; s < D / 16; ++s) {
+          sacc = mfma32(lds_row<D>(Kt, off, kk, s), qreg[s], sacc);
+          pacc = mfma32(lds_row<D>(Vt, off, kk, s), dreg[s], pacc);   // dP - delta
         }
         bf16x8 ka[2][D / 32];   // K^T operands, read before the dS arithmetic
 #pragma unroll
