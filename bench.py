@@ -37,8 +37,8 @@ PEAK_HBM_GBS = 8000.0
 # kernels in the same counter runs.  Valid only for the kernel source the
 # counters were taken on (hash of attn.hip + prism_device.h without comments);
 # reported as null for any other source or workload.
-FWD_TRAFFIC = dict(workload="2k", bytes=70_277_718 * 1024,
-                   source_sha256="bed312be8825b1b2374f124fc19b6e3e6985622318ae37ffbfd219733f8be240")
+FWD_TRAFFIC = dict(workload="2k", bytes=74_448_364 * 1024,
+                   source_sha256="5ea7b6a08db1c2460f77412e6eb69453f679b6df8b7cc5d024f23dfc0fa0dcfb")
 
 
 def attn_source_sha256(base: str | None = None) -> str:
@@ -361,8 +361,10 @@ def main():
     an = torch.empty(cfg.N, dtype=torch.float32, device=dev)
     a2v_norms(hh, an)
     # each repetition after a 512 MiB read (twice the 256 MB last-level cache,
-    # clean lines), so h-hat comes from HBM
-    flush = torch.ones(128 << 20, dtype=torch.int32, device=dev)
+    # clean lines), so h-hat comes from HBM.  float32: torch sums it in place
+    # (an int32 sum first writes a 1 GiB int64 copy, whose dirty lines would
+    # then be written back during the timed kernel)
+    flush = torch.ones(128 << 20, dtype=torch.float32, device=dev)
     ts = []
     for _ in range(10):
         flush.sum()
