@@ -651,7 +651,12 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(
       for (int kk = 0; kk < 2; ++kk)
 #pragma unroll
         for (int i = 0; i < 16; ++i) mloc = fmaxf(mloc, sacc[kk][i]);
-      mloc = fmaxf(mloc, __shfl_xor(mloc, 32, 64)) * sl2;
+      {
+        // the other 32-lane half's maximum through a VALU lane swap: a
+        // shuffle would be an LDS op queued behind the V^T reads above
+        const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mloc), __float_as_uint(mloc), false, false);
+        mloc = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1])) * sl2;
+      }
       if (__any(mloc > m_run + kRescale)) {
         const float m_new = fmaxf(m_run, mloc);
         const float alpha = fast_exp2(m_run - m_new);
