@@ -21,7 +21,9 @@
 //  * operand tiles live in HBM exactly as they sit in LDS (row-major, XOR
 //    swizzled 16-byte chunks), so staging is an asynchronous copy into LDS
 //    (buffer_load_dwordx4 ... lds, addressed from scalar registers),
-//    double-buffered behind the MFMA work;
+//    double-buffered behind the MFMA work; the forward's walk is software
+//    pipelined inside each wave (S of one tile and PV of the tile two back
+//    interleaved with the softmax of the tile between);
 //  * operands that need a tile's columns (V^T, K^T, Q^T, dO^T) are read from
 //    the same row tiles with the transposing LDS read ds_read_b64_tr_b16;
 //  * float32 online softmax in the log2 domain with lazy rescaling (the
@@ -556,6 +558,31 @@ __global__ void zero_kernel(int* __restrict__ p, int n) {
 // ---------------------------------------------------------------------------
 // forward
 // ---------------------------------------------------------------------------
+// Workgroup barrier without a memory fence: __syncthreads() would also wait
+// for every copy in flight (its release covers LDS written by the copies).
+// The loop's LDS reads are all consumed before the barrier and the explicit
+// wait before it orders the copies; the empty asm statements keep the
+// compiler from moving memory accesses across.
+__device__ __forceinline__ void barrier_nofence() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_sched_barrier(0);
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_sched_barrier(0);
+  asm volatile("" ::: "memory");
+}
+
+// Forward: each wave's walk over the key tiles is software pipelined three
+// deep.  Iteration j computes S(j) = K(j) Q^T and the PV product of tile
+// j - 2 as one-MFMA chunks (S and PV alternating), and between them the
+// softmax of tile j - 1, so the wave's own vector work runs while its matrix
+// products execute; the other workgroup on the CU fills the rest.  Stage
+// j & 1 holds K(j) and V(j - 2); after the barrier of iteration j the copy of
+// K(j + 1) and V(j - 1) goes into the other stage.  Per tile the running
+// output takes the same operations in the same order as a walk without the
+// pipeline: PV(t - 1) is added, then the rescale decided by the softmax of
+// t, then PV(t).
+constexpr int kReadAhead = 2;   // forward: chunks between an operand's LDS read and its MFMA
+
 template <int D, bool DENSE>
 __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(
     Geometry g, float sl2, const uint16_t* __restrict__ qp, const uint16_t* __restrict__ kp,
@@ -564,8 +591,8 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(
     uint16_t* __restrict__ o, uint16_t* __restrict__ o_lo, float* __restrict__ lse, int* __restrict__ cnt,
     const int32_t* __restrict__ order) {
   constexpr int TB = TileGeo<D>::BYTES;
-  __shared__ __attribute__((aligned(16))) char stage0[TileGeo<D>::STAGE];   // K, V of even steps
-  __shared__ __attribute__((aligned(16))) char stage1[TileGeo<D>::STAGE];   // K, V of odd steps
+  __shared__ __attribute__((aligned(16))) char stage0[TileGeo<D>::STAGE];   // K(j), V(j - 2) of even j
+  __shared__ __attribute__((aligned(16))) char stage1[TileGeo<D>::STAGE];   // K(j), V(j - 2) of odd j
   __shared__ int s_work;
   const int npair = (int)(g.tiles / 2);
   WorkQueue wq;
@@ -600,118 +627,160 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(
   float m_run = -INFINITY, l_run = 0.0f, r_run = 0.0f;
 
   PairIter it = make_iter(g, h, 2 * pair, 2 * pair + 1, blk_start, n_blocks, DENSE ? nullptr : row_ptr, col_idx);
-  int kt, kt_next = 0;
-  bool ua, ub, ua_n = false, ub_n = false;
-  bool have = it.next(kt, ua, ub);
-  if (have) {
-    dma_tile<D>(stage0, Kb + (int64_t)kt * kTile * D);
-    dma_tile<D>(stage0 + TB, Vb + (int64_t)kt * kTile * D);
+  // next tile of the walk: e = it exists, m = this wave's query tile attends
+  // to it; past the end t = 0 (tile 0 of the head: the source of copies made
+  // only so that every slot a masked product reads holds finite values)
+  auto fetch = [&](int& t, bool& e, bool& m) {
+    bool ua, ub;
+    e = it.next(t, ua, ub);
+    m = e && (second ? ub : ua);
+    if (!e) t = 0;
+  };
+  // pipeline state: tiles j (S), j - 1 (softmax, and its V copy), j - 2
+  // (PV); the look-ahead tile j + 1, whose K is copied during iteration j
+  int tS, t1, tX = 0;
+  bool eS, mS, e1, m1, eX = false, mX = false, eP = false;
+  fetch(tS, eS, mS);
+  fetch(t1, e1, m1);
+  dma_tile<D>(stage0, Kb + (int64_t)tS * kTile * D);
+  dma_tile<D>(stage0 + TB, Vb);
+  floatx16 sc[2][2];   // S^T of the tiles of even / odd index (two 32-key halves)
+  bf16x8 pw[2][4];     // their bf16 weights, the B operands of PV
+  // the first two iterations run the softmax and PV of tiles -1, -2 masked
+#pragma unroll
+  for (int b2 = 0; b2 < 2; ++b2) {
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) sc[b2][kk][i] = 0.0f;
+#pragma unroll
+    for (int v = 0; v < 4; ++v)
+#pragma unroll
+      for (int i = 0; i < 8; ++i) pw[b2][v][i] = (__bf16)0.0f;
   }
 
   auto step = [&](auto par) {
-    constexpr int B = decltype(par)::value;
-    const bool have_next = it.next(kt_next, ua_n, ub_n);
-    wait_dma();
-    __syncthreads();
-    if (have_next) {
+    constexpr int B = decltype(par)::value, X = B ^ 1;   // parities of j and j - 1
+    int t2;
+    bool e2, m2;
+    fetch(t2, e2, m2);                         // tile j + 2
+    wait_dma();                                // this wave's copies of K(j), V(j - 2) have landed
+    barrier_nofence();                         // ... and every wave's; stage B ^ 1 is free
+    {
       char* nx = PRISM_STAGE(B ^ 1, stage0, stage1);
-      dma_tile<D>(nx, Kb + (int64_t)kt_next * kTile * D);
-      dma_tile<D>(nx + TB, Vb + (int64_t)kt_next * kTile * D);
+      dma_tile<D>(nx, Kb + (int64_t)t1 * kTile * D);        // K(j + 1)
+      dma_tile<D>(nx + TB, Vb + (int64_t)tX * kTile * D);   // V(j - 1)
     }
-    if (second ? ub : ua) {
-      const char* Kt = PRISM_STAGE(B, stage0, stage1);
-      const char* Vt = Kt + TB;
-      floatx16 sacc[2];
+    const char* Kt = PRISM_STAGE(B, stage0, stage1);
+    const char* Vt = Kt + TB;
+    // a wave whose query tile does not attend to a tile still runs its
+    // products, masked through the data: that tile's softmax takes the
+    // maximum +inf, so its weights are 0 and PV adds exact zeros (the output
+    // accumulators never hold -0); the running maximum and sums stay as they are
+    const bool doX = eX && mX;
+    float alpha = 1.0f;
+    bool resc = false;
+    {
+      constexpr int NS = D / 8;   // S products (two 32-key halves x D/16 k-steps)
+      constexpr int NC = 2 * NS;  // chunks: S and PV products alternating
+      bf16x8 kop[NS], vop[NS];
+      auto read = [&](int c) {
+        const int i = c >> 1;
+        if ((c & 1) == 0) kop[i] = lds_row<D>(Kt, off, i & 1, i >> 1);
+        else vop[i] = lds_col<D>(Vt, off, i % (D / 32), i / (2 * (D / 32)), (i / (D / 32)) & 1);
+      };
 #pragma unroll
       for (int kk = 0; kk < 2; ++kk)
 #pragma unroll
-        for (int i = 0; i < 16; ++i) sacc[kk][i] = 0.0f;
-      // every K row operand of the step is read before the first product, so
-      // the products wait for the LDS once instead of once per pair
-      bf16x8 kr[2][D / 16];
+        for (int i = 0; i < 16; ++i) sc[B][kk][i] = 0.0f;
 #pragma unroll
-      for (int s = 0; s < D / 16; ++s)
-#pragma unroll
-        for (int kk = 0; kk < 2; ++kk) kr[kk][s] = lds_row<D>(Kt, off, kk, s);
+      for (int c = 0; c < kReadAhead; ++c) read(c);
+      float mloc = 0.0f, m_use = 0.0f, lsum = 0.0f, rsum = 0.0f;
+      const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
       __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-      for (int s = 0; s < D / 16; ++s)
-#pragma unroll
-        for (int kk = 0; kk < 2; ++kk) sacc[kk] = mfma32(kr[kk][s], qreg[s], sacc[kk]);
-      // V^T operands do not depend on P: issue their LDS reads before the softmax
-      bf16x8 va[2][2][D / 32];
-#pragma unroll
-      for (int kk = 0; kk < 2; ++kk)
-#pragma unroll
-        for (int hh = 0; hh < 2; ++hh)
-#pragma unroll
-          for (int u = 0; u < D / 32; ++u) va[kk][hh][u] = lds_col<D>(Vt, off, u, kk, hh);
-      float mloc = sacc[0][0];
-#pragma unroll
-      for (int kk = 0; kk < 2; ++kk)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) mloc = fmaxf(mloc, sacc[kk][i]);
-      {
-        // the other 32-lane half's maximum through a VALU lane swap: a
-        // shuffle would be an LDS op queued behind the V^T reads above
-        const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mloc), __float_as_uint(mloc), false, false);
-        mloc = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1])) * sl2;
-      }
-      if (__any(mloc > m_run + kRescale)) {
-        const float m_new = fmaxf(m_run, mloc);
-        const float alpha = fast_exp2(m_run - m_new);
-        l_run *= alpha;
-        r_run *= alpha;
-#pragma unroll
-        for (int u = 0; u < D / 32; ++u)
-#pragma unroll
-          for (int i = 0; i < 16; ++i) oacc[u][i] *= alpha;
-        m_run = m_new;
-      }
-      bf16x8 pb[4];
-      float lsum = 0.0f, rsum = 0.0f;
-#pragma unroll
-      for (int kk = 0; kk < 2; ++kk)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const float pv = fast_exp2(__builtin_fmaf(sacc[kk][i], sl2, -m_run));
-          lsum += pv;
-          pb[kk * 2 + (i >> 3)][i & 7] = (__bf16)pv;
+      for (int c = 0; c < NC; ++c) {
+        if (c + kReadAhead < NC) read(c + kReadAhead);
+        const int i = c >> 1;
+        if ((c & 1) == 0) sc[B][i & 1] = mfma32(kop[i], qreg[i >> 1], sc[B][i & 1]);
+        else {
+          const int kk = i / (2 * (D / 32)), hh = (i / (D / 32)) & 1, u = i % (D / 32);
+          oacc[u] = mfma32(vop[i], pw[B][kk * 2 + hh], oacc[u]);
         }
-      // O is normalised by the sum of the same bf16-rounded weights the PV
-      // product uses (two per v_dot2); the log-sum-exp keeps the float32 weights
-      const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
+        if (c == 0) {
+          mloc = sc[X][0][0];
 #pragma unroll
-      for (int v = 0; v < 4; ++v) {
-        rsum = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pb[v], pb[v], 0, 1), ones, rsum, false);
-        rsum = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pb[v], pb[v], 2, 3), ones, rsum, false);
-        rsum = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pb[v], pb[v], 4, 5), ones, rsum, false);
-        rsum = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pb[v], pb[v], 6, 7), ones, rsum, false);
+          for (int e = 0; e < 16; ++e) mloc = fmaxf(mloc, sc[X][0][e]);
+        } else if (c == 1) {
+#pragma unroll
+          for (int e = 0; e < 16; ++e) mloc = fmaxf(mloc, sc[X][1][e]);
+          const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mloc), __float_as_uint(mloc), false, false);
+          mloc = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1])) * sl2;
+          resc = __any(mloc > m_run + kRescale) & doX;
+          const float m_new = resc ? fmaxf(m_run, mloc) : m_run;
+          const float a = fast_exp2(m_run - m_new);
+          alpha = resc ? a : 1.0f;
+          {
+#pragma clang fp contract(off)
+            l_run *= alpha;
+            r_run *= alpha;
+          }
+          m_run = m_new;
+          m_use = doX ? m_run : INFINITY;
+        } else {
+#pragma unroll
+          for (int e = ((c - 2) * 32) / (NC - 2); e < ((c - 1) * 32) / (NC - 2); ++e) {
+            const int kk = e >> 4, ii = e & 15;
+            const float pv = fast_exp2(__builtin_fmaf(sc[X][kk][ii], sl2, -m_use));
+            lsum += pv;
+            pw[X][kk * 2 + (ii >> 3)][ii & 7] = (__bf16)pv;
+            asm volatile("" : "+v"(lsum));
+            if ((e & 7) == 7) {
+              const int v = e >> 3;
+              rsum = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pw[X][v], pw[X][v], 0, 1), ones, rsum, false);
+              rsum = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pw[X][v], pw[X][v], 2, 3), ones, rsum, false);
+              rsum = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pw[X][v], pw[X][v], 4, 5), ones, rsum, false);
+              rsum = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pw[X][v], pw[X][v], 6, 7), ones, rsum, false);
+              asm volatile("" : "+v"(rsum), "+v"(pw[X][v]));
+            }
+          }
+        }
+        __builtin_amdgcn_sched_barrier(0);
       }
-      l_run += lsum;
-      r_run += rsum;
-#pragma unroll
-      for (int kk = 0; kk < 2; ++kk)
-#pragma unroll
-        for (int hh = 0; hh < 2; ++hh)
-#pragma unroll
-          for (int u = 0; u < D / 32; ++u) oacc[u] = mfma32(va[kk][hh][u], pb[kk * 2 + hh], oacc[u]);
+      {
+#pragma clang fp contract(off)
+        l_run += lsum;
+        r_run += rsum;
+      }
     }
-    kt = kt_next;
-    ua = ua_n;
-    ub = ub_n;
-    have = have_next;
+    if (resc) {
+#pragma unroll
+      for (int u = 0; u < D / 32; ++u)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) oacc[u][i] *= alpha;
+    }
+    eP = eX;
+    eX = eS;
+    mX = mS;
+    tX = tS;
+    eS = e1;
+    mS = m1;
+    tS = t1;
+    t1 = t2;
+    e1 = e2;
+    m1 = m2;
   };
-  while (have) {
+  while (eS || eX || eP) {
     step(Parity<0>{});
-    if (!have) break;
+    if (!(eS || eX || eP)) break;
     step(Parity<1>{});
   }
+  wait_dma();   // the last copies have landed before stage0 becomes the staging area
+  __syncthreads();
 
   const float l_tot = l_run + __shfl_xor(l_run, 32, 64);
   const float inv = 1.0f / (r_run + __shfl_xor(r_run, 32, 64));
   if (lse != nullptr && g32 == 0) lse[hN + qt * kTile + rloc] = (m_run + __log2f(l_tot)) * kLn2;
-  __syncthreads();
   uint16_t* st = (uint16_t*)stage0;       // 128 x (D + 8) staging rows
   acc_to_stage<D>(st, oacc, 32 * w + l32, g32, inv);
   __syncthreads();
