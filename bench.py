@@ -37,8 +37,8 @@ PEAK_HBM_GBS = 8000.0
 # kernels in the same counter runs.  Valid only for the kernel source the
 # counters were taken on (hash of attn.hip + prism_device.h without comments);
 # reported as null for any other source or workload.
-FWD_TRAFFIC = dict(workload="2k", bytes=73_491_804 * 1024,
-                   source_sha256="66174d0a700681384154708510c64cdb56957b400df8e0cf93ef12ab1901f368")
+FWD_TRAFFIC = dict(workload="2k", bytes=67_010_902 * 1024,
+                   source_sha256="4178f7c19ef50fb22ab95c662e99cc9bf0ec5d4f108b5814bdaaa65fc04c217e")
 
 
 def attn_source_sha256(base: str | None = None) -> str:
@@ -197,18 +197,23 @@ def kernel_figures(step, stream, cfg, pairs: int, args) -> dict:
         ms = sum(ts)
         out[name] = dict(launches=len(ts), ms=round(ms, 4), bytes=int(b), gbps=round(b / (ms * 1e-3) / 1e9, 1),
                          frac_hbm=round(b / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4))
-    # executed MFMA work per selected token pair: forward S and PV; dQ pass
-    # S, dP and dQ; dK/dV pass S, dP, dV and dK
+    # MFMA work over the selected token pairs: forward S and PV; dQ pass S,
+    # dP and dQ; dK/dV pass S, dP, dV and dK.  The two backward passes
+    # execute exactly this; the forward also runs the tiles of its walk that
+    # one of its two query tiles does not attend to (masked) and two
+    # pipeline-drain iterations per work item: +1.7% at 2K by the MFMA
+    # instruction counters
     mfma = {"attn_fwd_kernel<%d, false>" % D: 4, "attn_bwd_dq_kernel<%d, false>" % D: 6,
             "attn_bwd_dkdv_kernel<%d, false>" % D: 8}
-    for name, executed in mfma.items():
+    for name, per_pair in mfma.items():
         ts = times.get(name)
         if not ts:
             continue
         ms = sum(ts)
-        f = executed * D * pairs
-        out[name] = dict(ms=round(ms, 4), executed_flops=f, executed_tflops=round(f / (ms * 1e-3) / 1e12, 1),
-                         executed_frac=round(f / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4))
+        f = per_pair * D * pairs
+        out[name] = dict(ms=round(ms, 4), pair_flops=f, basis=f"{per_pair}*D per selected token pair",
+                         tflops=round(f / (ms * 1e-3) / 1e12, 1),
+                         frac=round(f / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4))
     out["all_kernels_ms"] = round(sum(sum(v) for v in times.values()), 4)
     return out
 
