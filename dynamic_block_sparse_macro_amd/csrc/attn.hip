@@ -678,7 +678,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(
     // maximum +inf, so its weights are 0 and PV adds exact zeros (the output
     // accumulators never hold -0); the running maximum and sums stay as they are
     const bool doX = eX && mX;
-    float alpha = 1.0f;
+    float alpha = 1.0f, lsum = 0.0f, rsum = 0.0f;
     bool resc = false;
     {
       constexpr int NS = D / 8;   // S products (two 32-key halves x D/16 k-steps)
@@ -695,7 +695,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(
         for (int i = 0; i < 16; ++i) sc[B][kk][i] = 0.0f;
 #pragma unroll
       for (int c = 0; c < kReadAhead; ++c) read(c);
-      float mloc = 0.0f, m_use = 0.0f, lsum = 0.0f, rsum = 0.0f;
+      float mloc = 0.0f, m_use = 0.0f;
       const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
       __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
@@ -718,13 +718,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(
           mloc = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1])) * sl2;
           resc = __any(mloc > m_run + kRescale) & doX;
           const float m_new = resc ? fmaxf(m_run, mloc) : m_run;
-          const float a = fast_exp2(m_run - m_new);
-          alpha = resc ? a : 1.0f;
-          {
-#pragma clang fp contract(off)
-            l_run *= alpha;
-            r_run *= alpha;
-          }
+          alpha = fast_exp2(m_run - m_new);   // used only when resc
           m_run = m_new;
           m_use = doX ? m_run : INFINITY;
         } else {
@@ -747,17 +741,19 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(
         }
         __builtin_amdgcn_sched_barrier(0);
       }
-      {
-#pragma clang fp contract(off)
-        l_run += lsum;
-        r_run += rsum;
-      }
     }
-    if (resc) {
+    if (resc) {   // rare: the running sums and output move to the new maximum
+      l_run *= alpha;
+      r_run *= alpha;
 #pragma unroll
       for (int u = 0; u < D / 32; ++u)
 #pragma unroll
         for (int i = 0; i < 16; ++i) oacc[u][i] *= alpha;
+    }
+    {
+#pragma clang fp contract(off)
+      l_run += lsum;
+      r_run += rsum;
     }
     eP = eX;
     eX = eS;
