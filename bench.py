@@ -37,8 +37,8 @@ PEAK_HBM_GBS = 8000.0
 # kernels in the same counter runs.  Valid only for the kernel source the
 # counters were taken on (hash of attn.hip + prism_device.h without comments);
 # reported as null for any other source or workload.
-FWD_TRAFFIC = dict(workload="2k", bytes=66_881_114 * 1024,
-                   source_sha256="f2506ec6f4827ae913d441829cd94b126c5240de00d6b3d07da66b940ead5bc6")
+FWD_TRAFFIC = dict(workload="2k", bytes=66_826_880 * 1024,
+                   source_sha256="48d85c7fadaa062e4132843b9838c1c13eb9c2cf2d04c6c509273deac68e2a55")
 
 
 def attn_source_sha256(base: str | None = None) -> str:

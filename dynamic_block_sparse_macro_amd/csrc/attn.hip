@@ -838,6 +838,8 @@ __global__ __launch_bounds__(256) void bwd_pre_kernel(Geometry g, const uint16_t
 // ---------------------------------------------------------------------------
 // backward, query-major pass: dQ (in 32-key halves of each key tile)
 // ---------------------------------------------------------------------------
+constexpr int kReadAheadQ = 2;   // dQ pass: chunks between an operand's LDS read and its MFMA
+
 template <int D, bool DENSE>
 __global__ __launch_bounds__(kThreads, 2) void attn_bwd_dq_kernel(
     Geometry g, float scale, float sl2, const uint16_t* __restrict__ qp, const uint16_t* __restrict__ kp,
@@ -915,10 +917,23 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bwd_dq_kernel(
           sacc[i] = 0.0f;
           pacc[i] = nd;
         }
+        {
+          // one-MFMA chunks, K and V row operands read kReadAheadQ chunks
+          // ahead (left to itself the compiler reads each operand into the
+          // same registers right before its product and waits for it)
+          constexpr int NC = D / 8;   // S and dP products alternating
+          bf16x8 op[NC];
+          auto read = [&](int c) { op[c] = lds_row<D>((c & 1) ? Vt : Kt, off, kk, c >> 1); };
 #pragma unroll
-        for (int s = 0; s < D / 16; ++s) {
-          sacc = mfma32(lds_row<D>(Kt, off, kk, s), qreg[s], sacc);
-          pacc = mfma32(lds_row<D>(Vt, off, kk, s), dreg[s], pacc);   // dP - delta
+          for (int c = 0; c < kReadAheadQ; ++c) read(c);
+          __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+          for (int c = 0; c < NC; ++c) {
+            if (c + kReadAheadQ < NC) read(c + kReadAheadQ);
+            if ((c & 1) == 0) sacc = mfma32(op[c], qreg[c >> 1], sacc);
+            else pacc = mfma32(op[c], dreg[c >> 1], pacc);   // dP - delta
+            __builtin_amdgcn_sched_barrier(0);
+          }
         }
         bf16x8 ka[2][D / 32];   // K^T operands, read before the dS arithmetic
 #pragma unroll

@@ -43,6 +43,16 @@ __global__ __launch_bounds__(256) void zone_stats_kernel(Geometry g, const uint1
   const int cp = tid % LPT, grp = tid / LPT;
   const uint16_t* vb = v + (int64_t)h * g.hstride + 2 * cp;
 
+  // the zone's audio norms (64 threads x 8 values) are loaded first, so their
+  // latency overlaps that of the value loads
+  float apre[8];
+  if (tid < 64) {
+    const int eta = tid >> 3, om = tid & 7;
+#pragma unroll
+    for (int tau = 0; tau < 8; ++tau)
+      apre[tau] = a ? a[((int64_t)(zt * kZone + tau) * g.H + zh * kZone + eta) * g.W + zw * kZone + om] : 0.0f;
+  }
+
   double sT[TPG][2], sH[8][2], sW[8][2];
 #pragma unroll
   for (int i = 0; i < 8; ++i) sH[i][0] = sH[i][1] = sW[i][0] = sW[i][1] = 0.0;
@@ -100,11 +110,8 @@ __global__ __launch_bounds__(256) void zone_stats_kernel(Geometry g, const uint1
   // audio cube (a shared by all heads)
   if (tid < 64) {
     const int eta = tid >> 3, om = tid & 7;
-    for (int tau = 0; tau < 8; ++tau) {
-      double x = 0.0;
-      if (a) x = (double)a[((int64_t)(zt * kZone + tau) * g.H + zh * kZone + eta) * g.W + zw * kZone + om];
-      acube[(tau * 8 + eta) * 8 + om] = x;
-    }
+#pragma unroll
+    for (int tau = 0; tau < 8; ++tau) acube[(tau * 8 + eta) * 8 + om] = (double)apre[tau];
   }
 
   // per-channel variance of the slice means, per axis
@@ -145,8 +152,10 @@ __global__ __launch_bounds__(256) void zone_stats_kernel(Geometry g, const uint1
   }
   __syncthreads();
   if (tid == 0) {
+    // zone total from the eight T-slice sums (sums of float32 values are
+    // exact in float64, so the order of the additions does not matter)
     double tot = 0.0;
-    for (int i = 0; i < 512; ++i) tot += acube[i];
+    for (int i = 0; i < 8; ++i) tot += aslice[0][i] * 64.0;
     double sa[3];
     for (int d = 0; d < 3; ++d) {
       double mu = 0.0;
