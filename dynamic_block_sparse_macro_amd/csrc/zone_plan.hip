@@ -8,10 +8,12 @@
 // l*_d = -1/2 log2 g_d + 1/3 (log2 B + 1/2 sum_d' log2 g_d'); the block
 // shape is the candidate of that volume nearest to l* in log2 distance.
 //
-// All statistics and decisions in float64.  Sums of bfloat16 / float32 inputs
-// are exact in float64, so per-zone statistics do not depend on summation
-// order; this file is built without floating-point contraction so that the
-// decision arithmetic is the plain sequence of IEEE operations.
+// All statistics and decisions in float64.  A zone's sums of bfloat16 values
+// (512 terms within 36 binades of each other) and of float32 values (within 20
+// binades) are exact in float64, so per-zone statistics do not depend on
+// summation order for such inputs; this file is built without floating-point
+// contraction so that the decision arithmetic is the plain sequence of IEEE
+// operations.
 
 #include "prism_device.h"
 #include "prism_internal.h"
@@ -152,8 +154,8 @@ __global__ __launch_bounds__(256) void zone_stats_kernel(Geometry g, const uint1
   }
   __syncthreads();
   if (tid == 0) {
-    // zone total from the eight T-slice sums (sums of float32 values are
-    // exact in float64, so the order of the additions does not matter)
+    // zone total from the eight T-slice sums (exact, like the slice sums, for
+    // norms within 20 binades of each other, so the grouping does not matter)
     double tot = 0.0;
     for (int i = 0; i < 8; ++i) tot += aslice[0][i] * 64.0;
     double sa[3];
