@@ -31,6 +31,7 @@ sys.path.insert(0, ROOT)
 
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
 PEAK_HBM_GBS = 8000.0
+PEAK_SCLK_GHZ = 2.4   # the shader clock the published MFMA peak is quoted at
 
 # HBM bytes per launch of attn_fwd_kernel at the 2K workload (both heads):
 # FETCH_SIZE x 2.000 + WRITE_SIZE, the factors read from plain 1 GiB copy
@@ -320,9 +321,14 @@ def main():
     log(f"density {density:.4f}, attention {attn_tflops:.1f} TFLOP/s (fwd {fwd_tflops:.1f}, bwd {bwd_tflops:.1f})")
 
     kernels = None
+    sclk = None
     if not args.no_kernel_times:
         kernels = kernel_figures(step, stream, cfg, P, args)
         log("kernels", json.dumps(kernels))
+        # shader clock under a sustained MFMA stream (median of 3 probes): the
+        # peak the kernels can approach is the published one scaled by it
+        sclk = float(np.median([B.prism_sclk_probe(stream) for _ in range(3)]))
+        log(f"shader clock under MFMA load {sclk:.3f} GHz")
 
     dense = None
     if not args.no_dense:
@@ -454,6 +460,10 @@ def main():
                     executed_flops_per_call=14 * D * P, executed_frac=round(14 * D * P / (bwd_ms * 1e-3) / 1e12
                                                                             / PEAK_BF16_TFLOPS, 4),
                     call_ms=round(bwd_ms, 4))
+    if sclk is not None:
+        peak_sclk = PEAK_BF16_TFLOPS * sclk / PEAK_SCLK_GHZ
+        for r, tf in ((roof, fwd_tflops), (roof_bwd, bwd_tflops)):
+            r.update(sclk_ghz=round(sclk, 3), peak_at_sclk=round(peak_sclk, 1), frac_at_sclk=round(tf / peak_sclk, 4))
     line = {
         "metric": "fwd+bwd ms per head at 450K tokens; achieved MFMA TFLOP/s (% of peak)",
         "value": round(ms_step / heads, 3),

@@ -34,7 +34,7 @@ VARIANT_RHO_MAX_AUDIO = 32
 
 ENTRY_POINTS = ("prism_zone_stats", "prism_plan_shapes", "prism_select_blocks", "prism_attn_fwd",
                 "prism_attn_bwd", "prism_dense_attn_fwd", "prism_dense_attn_bwd", "prism_a2v_norms", "prism_infer_fwd",
-                "prism_check_index", "prism_attn_fwd_noalloc", "prism_strerror")
+                "prism_check_index", "prism_attn_fwd_noalloc", "prism_sclk_probe", "prism_strerror")
 
 
 class PrismError(RuntimeError):
@@ -94,6 +94,7 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         "prism_infer_fwd": [pp, pr, _vp, _vp, _vp, _vp, _vp, _vp, _P(ctypes.c_size_t), _vp],
         "prism_check_index": [pp] + [_vp] * 7 + [ctypes.c_int64, _vp],
         "prism_attn_fwd_noalloc": [pp, pr] + [_vp] * 12,
+        "prism_sclk_probe": [_P(ctypes.c_double), _vp],
     }
     for name, args in sig.items():
         f = getattr(lib, name)
@@ -210,6 +211,13 @@ def prism_infer_fwd(prob, par, q, k, v, a, o, ws, ws_bytes, stream=None, check=T
     st = load_library().prism_infer_fwd(ctypes.byref(prob), ctypes.byref(par), _ptr(q), _ptr(k), _ptr(v), _ptr(a),
                                         _ptr(o), _ptr(ws), _ref(ws_bytes), _stream(stream))
     return _check("prism_infer_fwd", st) if check else st
+
+
+def prism_sclk_probe(stream=None) -> float:
+    """Shader clock (GHz) under a sustained MFMA load; synchronises the stream."""
+    ghz = ctypes.c_double(0.0)
+    _check("prism_sclk_probe", load_library().prism_sclk_probe(ctypes.byref(ghz), _stream(stream)))
+    return ghz.value
 
 
 def prism_check_index(prob, perm, blk_start, n_blocks, row_ptr, col_idx, t_row_ptr, t_col_idx, n_idx, bad=None,

@@ -336,6 +336,19 @@ int prism_check_index(const prism_problem *prob, const int32_t *perm, const int3
                       const int32_t *row_ptr, const int32_t *col_idx, const int32_t *t_row_ptr,
                       const int32_t *t_col_idx, int64_t n_idx, int64_t *bad);
 
+/*
+ * prism_sclk_probe -- the shader clock the chip holds under a sustained
+ * matrix-core load (a measurement aid for stating MFMA rates against the
+ * peak at the clock actually run, not a step of the method).  Runs about
+ * 8 ms of independent bf16 MFMAs at two waves per SIMD on every CU and
+ * compares the shader-clock counter with the constant 100 MHz counter.
+ * ghz  HOST double (out): the clock in GHz.
+ * Synchronises `stream`.  Uses a 64 KiB array in the library's module
+ * memory (allocates nothing); calls that overlap on one GPU race.  Returns
+ * PRISM_EINVAL for a NULL pointer, PRISM_EHIP for a runtime error.
+ */
+int prism_sclk_probe(double *ghz, prism_stream stream);
+
 /* Human-readable text of a status code (static storage). */
 const char *prism_strerror(int status);
 
