@@ -9,11 +9,11 @@ tiles, the two tiles of a pair attending to disjoint key blocks (every step
 computed by one wave pair and masked for the other), one list nested in its
 neighbour's, rows over every block, every other block, and a few random
 blocks.  Blocks are 64 tokens everywhere (fixed shape 0), so the two tiles
-of every pair are different blocks, and, in a second case, the layer's own
-mixed 64/128/256-token partition.  Forward, LSE and the three gradients are
-compared with the oracle on the same lists (Prism pt reading guide, Método 3:
-attention over the selected blocks only; zh guide, 常见问题: gradients
-through the selected blocks only).
+of every pair are different blocks (at head_dim 128 and 64), and, in a
+further case, the layer's own mixed 64/128/256-token partition.  Forward,
+LSE and the three gradients are compared with the oracle on the same lists
+(Prism pt reading guide, Método 3: attention over the selected blocks only;
+zh guide, 常见问题: gradients through the selected blocks only).
 """
 
 import math
@@ -65,13 +65,13 @@ def csr(rows: list[list[int]]) -> tuple[np.ndarray, np.ndarray]:
     return row_ptr, np.concatenate([np.asarray(r, np.int64) for r in rows])
 
 
-@pytest.mark.parametrize("case", ["single_tile_blocks", "layer_blocks"])
+@pytest.mark.parametrize("case", ["single_tile_blocks", "layer_blocks", "single_tile_blocks_d64"])
 def test_hand_built_walks(case):
     import torch
     from dynamic_block_sparse_macro_amd import binding as B
-    wl = generate("par_small")
+    wl = generate("par_d64" if case.endswith("_d64") else "par_small")
     c = wl.cfg
-    if case == "single_tile_blocks":
+    if case.startswith("single_tile_blocks"):
         par = B.make_params(top_k=c.top_k, top_p=c.top_p, density_cap=c.density_cap,
                             variant=O.VARIANT_FIXED_SHAPE, fixed_shape=0)
     else:
