@@ -94,17 +94,27 @@ struct TileGeo {
 // no vector ALU work.
 constexpr int kRsrcFlags = 0x00020000;   // descriptor word 3: 32-bit data format
 
+// buffer resource covering one contiguous operand tile
+template <int D>
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t tile_rsrc(const uint16_t* src) {
+  return __builtin_amdgcn_make_buffer_rsrc((void*)src, (short)0, TileGeo<D>::BYTES, kRsrcFlags);
+}
+// copy instructions per wave of one tile copy
+template <int D>
+constexpr int kCopyOpsOf = TileGeo<D>::CHUNKS / kThreads;
+// instruction `op` of this wave's share of an asynchronous tile copy into LDS
+template <int D>
+__device__ __forceinline__ void dma_tile_op(__amdgpu_buffer_rsrc_t r, char* lds, int op) {
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
+  const int chunk0 = op * kThreads + w * 64;
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)(lds + chunk0 * 16), 16, lane * 16, chunk0 * 16, 0, 0);
+}
 // asynchronous copy of one contiguous operand tile into LDS (all 256 threads)
 template <int D>
 __device__ __forceinline__ void dma_tile(char* lds, const uint16_t* __restrict__ src) {
-  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
-  const __amdgpu_buffer_rsrc_t r =
-      __builtin_amdgcn_make_buffer_rsrc((void*)src, (short)0, TileGeo<D>::BYTES, kRsrcFlags);
+  const __amdgpu_buffer_rsrc_t r = tile_rsrc<D>(src);
 #pragma unroll
-  for (int it = 0; it < TileGeo<D>::CHUNKS / kThreads; ++it) {
-    const int chunk0 = it * kThreads + w * 64;
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)(lds + chunk0 * 16), 16, lane * 16, chunk0 * 16, 0, 0);
-  }
+  for (int op = 0; op < kCopyOpsOf<D>; ++op) dma_tile_op<D>(r, lds, op);
 }
 // asynchronous copy of 64 floats (one per tile row) into LDS
 // (called by one whole wave; lane l copies float l)
@@ -582,6 +592,7 @@ __device__ __forceinline__ void barrier_nofence() {
 // pipeline: PV(t - 1) is added, then the rescale decided by the softmax of
 // t, then PV(t).
 constexpr int kReadAhead = 2;   // forward: chunks between an operand's LDS read and its MFMA
+constexpr int kCopyStride = 4;   // forward: chunks between two copy instructions
 
 template <int D, bool DENSE>
 __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(
@@ -666,11 +677,13 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(
     fetch(t2, e2, m2);                         // tile j + 2
     wait_dma();                                // this wave's copies of K(j), V(j - 2) have landed
     barrier_nofence();                         // ... and every wave's; stage B ^ 1 is free
-    {
-      char* nx = PRISM_STAGE(B ^ 1, stage0, stage1);
-      dma_tile<D>(nx, Kb + (int64_t)t1 * kTile * D);        // K(j + 1)
-      dma_tile<D>(nx + TB, Vb + (int64_t)tX * kTile * D);   // V(j - 1)
-    }
+    // copies of K(j + 1) and V(j - 1) into the other stage: one copy
+    // instruction every kCopyStride chunks of the loop below, so that the
+    // first products of the iteration are not queued behind them
+    char* const nx = PRISM_STAGE(B ^ 1, stage0, stage1);
+    const __amdgpu_buffer_rsrc_t rk = tile_rsrc<D>(Kb + (int64_t)t1 * kTile * D);
+    const __amdgpu_buffer_rsrc_t rv = tile_rsrc<D>(Vb + (int64_t)tX * kTile * D);
+    constexpr int kCopyOps = kCopyOpsOf<D>;
     const char* Kt = PRISM_STAGE(B, stage0, stage1);
     const char* Vt = Kt + TB;
     // a wave whose query tile does not attend to a tile still runs its
@@ -700,6 +713,10 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(
       __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int c = 0; c < NC; ++c) {
+        if (c % kCopyStride == 0 && c / kCopyStride < 2 * kCopyOps) {
+          const int ci = c / kCopyStride, tile = ci / kCopyOps;   // tile 0: K(j + 1), 1: V(j - 1)
+          dma_tile_op<D>(tile ? rv : rk, nx + tile * TB, ci % kCopyOps);
+        }
         if (c + kReadAhead < NC) read(c + kReadAhead);
         const int i = c >> 1;
         if ((c & 1) == 0) sc[B][i & 1] = mfma32(kop[i], qreg[i >> 1], sc[B][i & 1]);
