@@ -143,6 +143,59 @@ __device__ T block_exclusive_scan(T x, T* wtot, T* total) {
   return off + inc - x;
 }
 
+// The rank-th smallest (1-based) of the distinct keys keys[0, nb): eight
+// passes over 8-bit digits, most significant first, each counting the keys
+// that still match the digits fixed so far in an LDS histogram.
+__device__ uint64_t radix_select(const uint64_t* keys, int nb, int rank, int* hist, int* sel) {
+  const int tid = threadIdx.x, nt = blockDim.x;
+  uint64_t prefix = 0, pmask = 0;
+  for (int shift = 56; shift >= 0; shift -= 8) {
+    for (int i = tid; i < 256; i += nt) hist[i] = 0;
+    __syncthreads();
+    for (int j = tid; j < nb; j += nt) {
+      const uint64_t k = keys[j];
+      if ((k & pmask) == prefix) atomicAdd(&hist[(int)((k >> shift) & 255u)], 1);
+    }
+    __syncthreads();
+    if (tid < 64) {   // one wave: the digit whose bucket holds the rank-th key
+      int c[4], sum = 0;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        c[i] = hist[4 * tid + i];
+        sum += c[i];
+      }
+      int inc = sum;
+#pragma unroll
+      for (int o = 1; o < 64; o <<= 1) {
+        const int y = __shfl_up(inc, o, 64);
+        if (tid >= o) inc += y;
+      }
+      const int exc = inc - sum;
+      if (rank > exc && rank <= inc) {
+        int r = rank - exc, b = 4 * tid + 3;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          if (r <= c[i]) {
+            b = 4 * tid + i;
+            break;
+          }
+          r -= c[i];
+        }
+        sel[0] = b;
+        sel[1] = r;
+      }
+    }
+    __syncthreads();
+    prefix |= (uint64_t)sel[0] << shift;
+    pmask |= 255ull << shift;
+    rank = sel[1];
+    __syncthreads();   // sel and hist are rewritten by the next pass
+  }
+  return prefix;
+}
+
+constexpr int kSelectMaxKeysPerThread = 16384 / kSelectThreads;   // the largest row, in LDS
+
 __global__ __launch_bounds__(kSelectThreads) void select_kernel(const double* __restrict__ S, int64_t ldS, int nb, int npow2,
                                                       int row0, const int32_t* __restrict__ bs, int top_k,
                                                       double top_p, double cap, int64_t N, int variant,
@@ -172,11 +225,43 @@ __global__ __launch_bounds__(kSelectThreads) void select_kernel(const double* __
   for (int w = tid; w < nbw; w += nt) bits[w] = 0u;
   const double Z = block_reduce(z, redd, OpAdd());
 
+  // Under a density cap only the first U / 64 positions of the sorted order
+  // can be selected (every block holds at least one 64-token tile), besides
+  // the top k: the M smallest keys are found by a radix select, moved to the
+  // front and sorted; the rest is never read.  The sorted prefix is the same
+  // as that of a sort of the whole row.
+  int nsort = npow2, nvalid = nb;
+  if (cap < 1.0) {
+    const int64_t U = (int64_t)floor(cap * (double)N);
+    const int mcap = (int)(U / kTile < (int64_t)nb ? U / kTile : (int64_t)nb);
+    const int M = max(min(top_k, nb), mcap);
+    int m2 = 1;
+    while (m2 < M) m2 <<= 1;
+    if (m2 < npow2 && M > 0) {
+      __shared__ int s_hist[256], s_sel[2], s_cnt;
+      const uint64_t T = radix_select(keys, nb, M, s_hist, s_sel);
+      uint64_t kv[kSelectMaxKeysPerThread];
+#pragma unroll
+      for (int i = 0; i < kSelectMaxKeysPerThread; ++i) {
+        const int j = tid + i * nt;
+        kv[i] = j < nb ? keys[j] : ~0ull;
+      }
+      if (tid == 0) s_cnt = 0;
+      __syncthreads();
+#pragma unroll
+      for (int i = 0; i < kSelectMaxKeysPerThread; ++i)
+        if (tid + i * nt < nb && kv[i] <= T) keys[atomicAdd(&s_cnt, 1)] = kv[i];
+      for (int q = M + tid; q < m2; q += nt) keys[q] = ~0ull;
+      nsort = m2;
+      nvalid = M;
+    }
+  }
+
   // bitonic sort, ascending
-  for (int k = 2; k <= npow2; k <<= 1) {
+  for (int k = 2; k <= nsort; k <<= 1) {
     for (int jj = k >> 1; jj > 0; jj >>= 1) {
       __syncthreads();
-      for (int t = tid; t < (npow2 >> 1); t += nt) {
+      for (int t = tid; t < (nsort >> 1); t += nt) {
         const int i = 2 * t - (t & (jj - 1));
         const int ixj = i + jj;
         const uint64_t a = keys[i], b = keys[ixj];
@@ -188,8 +273,10 @@ __global__ __launch_bounds__(kSelectThreads) void select_kernel(const double* __
   __syncthreads();
 
   // prefix mass C(n) and prefix key tokens T(n) in sorted order
+  // (chunks over the whole row, so that the sums over the first positions are
+  // grouped as in a full sort)
   const int chunk = (nb + nt - 1) / nt;
-  const int r0 = tid * chunk, r1 = min(nb, r0 + chunk);
+  const int r0 = tid * chunk, r1 = min(nvalid, r0 + chunk);
   double pl = 0.0;
   int64_t tl = 0;
   for (int q = r0; q < r1; ++q) {
