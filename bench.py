@@ -38,7 +38,7 @@ PEAK_SCLK_GHZ = 2.4   # the shader clock the published MFMA peak is quoted at
 # kernels in the same counter runs.  Valid only for the kernel source the
 # counters were taken on (hash of attn.hip + prism_device.h without comments);
 # reported as null for any other source or workload.
-FWD_TRAFFIC = dict(workload="2k", bytes=64_793_038 * 1024,
+FWD_TRAFFIC = dict(workload="2k", bytes=65_086_028 * 1024,
                    source_sha256="0da91f5fc95d36268f2a2336c12c3162d2fefbd41f7b3c73f8e9baec7412f1a6")
 
 
