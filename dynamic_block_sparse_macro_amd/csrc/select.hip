@@ -237,7 +237,7 @@ __global__ __launch_bounds__(kSelectThreads) void select_kernel(const double* __
     const int M = max(min(top_k, nb), mcap);
     int m2 = 1;
     while (m2 < M) m2 <<= 1;
-    if (m2 < npow2 && M > 0) {
+    if (m2 < npow2 && M > 0 && nb <= kSelectMaxKeysPerThread * nt) {   // (every row fits: N <= 2^20)
       __shared__ int s_hist[256], s_sel[2], s_cnt;
       const uint64_t T = radix_select(keys, nb, M, s_hist, s_sel);
       uint64_t kv[kSelectMaxKeysPerThread];
