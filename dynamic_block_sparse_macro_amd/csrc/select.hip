@@ -83,13 +83,27 @@ __global__ __launch_bounds__(256) void score_kernel(const double* __restrict__ q
   const int r0 = blockIdx.y * 64, j0 = blockIdx.x * 64;
   if (r0 >= rows || j0 >= nb) return;
   double acc[4][4] = {};
+  // this thread's four elements of each 64 x 16 chunk; the next chunk's are
+  // loaded while the current one is multiplied
+  double pa[4], pb[4];
+  auto load = [&](int c0) {
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int e = threadIdx.x + u * 256, rr = e >> 4, kk = e & 15;
+      pa[u] = (r0 + rr < rows) ? qbar[(int64_t)(row0 + r0 + rr) * D + c0 + kk] : 0.0;
+      pb[u] = (j0 + rr < nb) ? kbar[(int64_t)(j0 + rr) * D + c0 + kk] : 0.0;
+    }
+  };
+  load(0);
   for (int c0 = 0; c0 < D; c0 += 16) {
-    for (int e = threadIdx.x; e < 64 * 16; e += 256) {
-      const int rr = e >> 4, kk = e & 15;
-      As[kk][rr] = (r0 + rr < rows) ? qbar[(int64_t)(row0 + r0 + rr) * D + c0 + kk] : 0.0;
-      Bs[kk][rr] = (j0 + rr < nb) ? kbar[(int64_t)(j0 + rr) * D + c0 + kk] : 0.0;
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int e = threadIdx.x + u * 256, rr = e >> 4, kk = e & 15;
+      As[kk][rr] = pa[u];
+      Bs[kk][rr] = pb[u];
     }
     __syncthreads();
+    if (c0 + 16 < D) load(c0 + 16);
 #pragma unroll
     for (int kk = 0; kk < 16; ++kk) {
       double av[4], bv[4];
