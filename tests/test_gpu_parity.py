@@ -61,6 +61,12 @@ EXTREMES = [
     ("par_small", dict(top_k=1_000_000)),
     ("par_cap", dict(top_k=1, top_p=1e-9, density_cap=1e-6)),
     ("par_d64", dict(top_k=1, top_p=1e-9, variant=O.VARIANT_TOPP_ONLY)),
+    # under a cap the GPU sorts only the keys up to rank max(k, cap N / 64):
+    # a cap rank far below the row length, a top k above the cap rank, and a
+    # cap rank near the row's power of two
+    ("par_small", dict(density_cap=0.1)),
+    ("par_small", dict(density_cap=0.3, top_k=60)),
+    ("par_small", dict(density_cap=0.45)),
 ]
 
 
